@@ -1,0 +1,327 @@
+"""Plain CPU reference of one masked-diffusion decode step -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this module.  It shares no code with the HIP path
+and imports nothing from it.  Inputs are plain numpy arrays; bfloat16 data
+arrives as uint16 bit patterns and is widened here on its own.
+
+What one step computes, and where it comes from.  The pages are four news
+pages about dInfer; the mechanisms are only on the Traditional-Chinese
+explainer of arXiv 2510.08666 hosted on 91haoming.cn ("the explainer"):
+
+* the decoding-strategy component of the explainer fixes a position's
+  token "according to the AI's confidence in the text at each position":
+  this presupposes, per position, a candidate token and a confidence.  The
+  candidate is the arg-max of the logits ``z = h W^T`` of the vocabulary
+  head, the confidence the largest softmax probability ``1 / sum_v
+  exp(z_v - max z)``;
+* threshold decoding (same component, first strategy): fix at once every
+  masked position whose confidence is high enough, keep "thinking" about
+  the others;
+* hierarchical decoding (second strategy): split the regions still to be
+  filled recursively into sub-regions and fix the centre of each region
+  first;
+* credit decoding (third strategy): keep, for every position and every
+  candidate, a credit that grows when the candidate is chosen again with
+  confidence; stable candidates then commit more easily;
+* the diffusion-iteration manager paragraph: fixed-size blocks are handled
+  in turn (the block of L positions is the unit of one step).
+
+The pages give no number (threshold, decay, slot count, tie rule); those
+come from the workload definitions and the readings listed in the design
+notes (R1..R18): every row of the block goes through the head (R1); lowest
+token id wins an arg-max tie (R2); ``conf >= tau`` commits (R3); forced picks
+take the lowest position on ties (R4, R12, R15); an empty mask commits
+nothing (R7); an even span's centre is ``(s + e) // 2`` (R8); credit is
+updated before it is tested (R9); decay-then-add (R10); a candidate not in a
+slot evicts the first empty slot, else the smallest credit, lowest slot on
+ties (R11); the committed token is the current arg-max (R13); a span is split
+only when its centre commits (R14); credit changes only on masked rows (R16);
+``out_tokens`` holds the candidate of every row (R17).
+
+Precision.  Logits and the softmax sum are float64 over the exact input
+values (bfloat16 products are exact).  Where a float decides an integer the
+decision is taken in the kernel's precision: the logits are rounded to
+float32 before the arg-max / second-best, and confidences, credits and
+scores are float32 values compared against float32 thresholds, with each
+credit operation rounded to float32 as the state is stored in float32.
+
+Pins (tests/test_oracle_*.py): closed forms (zero hidden state, two-token
+vocabulary, hand-built logits with known softmax), brute-force loops on tiny
+shapes, permutation and shift properties, exact ties, the planted-peak
+limit, hand-worked commit sequences for all three strategies
+(tests/golden/), and the block invariants (monotone mask, each position
+committed once, at least one commit per step).
+"""
+from __future__ import annotations
+
+from typing import Iterable, Sequence
+
+import numpy as np
+
+THRESHOLD, HIERARCHICAL, CREDIT = 0, 1, 2
+SLOTS = 4          # tracked (token, credit) candidates per position
+EMPTY = -1         # token id of an unused credit slot
+
+_F32 = np.float32
+
+
+# --------------------------------------------------------------------------------------------
+# Inputs
+# --------------------------------------------------------------------------------------------
+def as_f64(x: np.ndarray) -> np.ndarray:
+    """Exact float64 values of float32 data or of bfloat16 bit patterns (uint16)."""
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        # a bfloat16 value is the float32 whose upper half is the pattern
+        return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if x.dtype == np.float32 or x.dtype == np.float64:
+        return x.astype(np.float64)
+    raise TypeError(f"unsupported input dtype {x.dtype}")
+
+
+# --------------------------------------------------------------------------------------------
+# LM head and per-position statistics
+# --------------------------------------------------------------------------------------------
+def lm_head_logits(hidden: np.ndarray, W: np.ndarray, vocab_chunk: int = 8192) -> np.ndarray:
+    """``z[r, v] = sum_k h[r, k] * W[v, k]`` in float64 for every row ``r`` (R1: all rows).
+
+    ``hidden`` is ``[M][H]``, ``W`` is ``[V][H]``; the matmul is a library
+    step, done over vocabulary chunks only to bound memory.
+    """
+    h = as_f64(hidden)
+    V = W.shape[0]
+    z = np.empty((h.shape[0], V), dtype=np.float64)
+    for v0 in range(0, V, vocab_chunk):
+        z[:, v0:v0 + vocab_chunk] = h @ as_f64(W[v0:v0 + vocab_chunk]).T
+    return z
+
+
+def token_stats(hidden: np.ndarray, W: np.ndarray, row_chunk: int = 64) -> dict:
+    """Candidate token, confidence and top-2 gap of every row.
+
+    * ``tok``  = lowest token id among the maxima of the float32-rounded logits (R2);
+    * ``gap``  = top logit minus the second-largest logit, counted with
+      multiplicity (an exact tie gives 0; a one-token vocabulary gives +inf);
+    * ``conf`` = ``1 / sum_v exp(z_v - max z)`` in float64, returned as float32:
+      the largest softmax probability (R5).
+    """
+    hidden = np.asarray(hidden)
+    H = W.shape[1]
+    h2 = hidden.reshape(-1, H)
+    M = h2.shape[0]
+    conf = np.empty(M, dtype=np.float32)
+    tok = np.empty(M, dtype=np.int64)
+    gap = np.empty(M, dtype=np.float32)
+    for r0 in range(0, M, row_chunk):
+        z = lm_head_logits(h2[r0:r0 + row_chunk], W)
+        rows = np.arange(z.shape[0])
+        z32 = z.astype(np.float32)
+        t = np.argmax(z32, axis=1)                     # first maximum = lowest id
+        top = z32[rows, t]
+        rest = z32.copy()
+        rest[rows, t] = -np.inf
+        second = rest.max(axis=1) if z.shape[1] > 1 else np.full(z.shape[0], -np.inf, np.float32)
+        gap[r0:r0 + z.shape[0]] = (top.astype(np.float64) - second.astype(np.float64)).astype(np.float32)
+        zmax = z.max(axis=1)
+        S = np.exp(z - zmax[:, None]).sum(axis=1)
+        conf[r0:r0 + z.shape[0]] = (1.0 / S).astype(np.float32)
+        tok[r0:r0 + z.shape[0]] = t
+    shape = hidden.shape[:-1]
+    return {"conf": conf.reshape(shape), "tok": tok.reshape(shape), "gap": gap.reshape(shape)}
+
+
+# --------------------------------------------------------------------------------------------
+# Commit strategies (one sequence: arrays of length L)
+# --------------------------------------------------------------------------------------------
+def _best(values: Sequence[float], positions: Sequence[int]) -> int:
+    """Position of the largest value; the lowest position wins a tie."""
+    best_p, best_v = None, None
+    for p, v in sorted(zip(positions, values)):
+        if best_v is None or _F32(v) > best_v:
+            best_p, best_v = p, _F32(v)
+    return best_p
+
+
+def _masked(mask: np.ndarray) -> list:
+    return [l for l in range(len(mask)) if mask[l]]
+
+
+def commit_threshold(conf: np.ndarray, mask: np.ndarray, tau: float) -> np.ndarray:
+    """Threshold decoding (explainer, decoding-strategy component, first strategy).
+
+    Every masked position with ``conf >= tau`` (R3) is fixed; when none is,
+    the single most confident masked position is (lowest position on ties,
+    R4).  No masked position: nothing is fixed (R7).
+    """
+    L = len(conf)
+    U = _masked(mask)
+    C = [l for l in U if _F32(conf[l]) >= _F32(tau)]
+    if not C and U:
+        C = [_best([conf[l] for l in U], U)]
+    out = np.zeros(L, dtype=bool)
+    out[C] = True
+    return out
+
+
+def _runs(mask: np.ndarray) -> list:
+    """Maximal runs ``(s, e)`` (inclusive) of masked positions, left to right."""
+    runs, l, L = [], 0, len(mask)
+    while l < L:
+        if mask[l]:
+            s = l
+            while l + 1 < L and mask[l + 1]:
+                l += 1
+            runs.append((s, l))
+        l += 1
+    return runs
+
+
+def commit_hierarchical(conf: np.ndarray, mask: np.ndarray, tau: float, max_depth: int = 0) -> np.ndarray:
+    """Hierarchical decoding (explainer, decoding-strategy component, second strategy).
+
+    The regions still to fill are the maximal masked runs.  A worklist
+    takes a run ``(s, e)``, looks at its centre ``c = (s + e) // 2`` (R8) and,
+    if ``conf[c] >= tau``, fixes ``c`` and puts the two halves ``(s, c-1)``
+    and ``(c+1, e)`` back on the list; a run whose centre is not confident
+    is left for a later iteration (R14).  ``max_depth > 0`` stops splitting
+    below that depth (the runs themselves are depth 1).  If nothing was
+    fixed, the most confident centre of a top-level run is (R15).
+    """
+    L = len(conf)
+    out = np.zeros(L, dtype=bool)
+    runs = _runs(mask)
+    work = [(s, e, 1) for (s, e) in runs]
+    while work:
+        s, e, depth = work.pop()
+        c = (s + e) // 2
+        if _F32(conf[c]) >= _F32(tau):
+            out[c] = True
+            if max_depth == 0 or depth < max_depth:
+                if s <= c - 1:
+                    work.append((s, c - 1, depth + 1))
+                if c + 1 <= e:
+                    work.append((c + 1, e, depth + 1))
+    if not out.any() and runs:
+        centres = [(s + e) // 2 for (s, e) in runs]
+        out[_best([conf[c] for c in centres], centres)] = True
+    return out
+
+
+def commit_credit(conf: np.ndarray, tok: np.ndarray, mask: np.ndarray,
+                  slot_tok: np.ndarray, slot_cr: np.ndarray, decay: float, theta: float):
+    """Credit decoding (explainer, decoding-strategy component, third strategy).
+
+    For every masked position ``l`` (R16), with ``SLOTS`` tracked candidates:
+
+    1. every slot's credit is multiplied by ``decay`` (R10);
+    2. if the current candidate ``tok[l]`` holds a slot, ``conf[l]`` is added
+       to that slot; otherwise it takes the first empty slot, else the slot
+       with the smallest credit (lowest slot on ties), with credit
+       ``0 + conf[l]`` (R11);
+    3. ``score = conf * (1 + credit of tok[l])`` with the updated credit (R9).
+
+    Masked positions with ``score >= theta`` are fixed with token ``tok[l]``
+    (R13); if none is, the highest score is (lowest position on ties, R12).
+    Returns ``(commit, slot_tok, slot_cr, score)``; the slot arrays are new.
+    """
+    L = len(conf)
+    st = np.array(slot_tok, dtype=np.int32, copy=True)
+    sc = np.array(slot_cr, dtype=np.float32, copy=True)
+    score = np.full(L, -np.inf, dtype=np.float32)
+    d = _F32(decay)
+    U = _masked(mask)
+    for l in U:
+        c = _F32(conf[l])
+        for i in range(SLOTS):
+            sc[l, i] = _F32(sc[l, i] * d)
+        held = [i for i in range(SLOTS) if st[l, i] == tok[l]]
+        if held:
+            i = held[0]
+            sc[l, i] = _F32(sc[l, i] + c)
+        else:
+            empty = [i for i in range(SLOTS) if st[l, i] == EMPTY]
+            if empty:
+                i = empty[0]
+            else:
+                i = min(range(SLOTS), key=lambda j: (sc[l, j], j))
+            st[l, i] = tok[l]
+            sc[l, i] = _F32(_F32(0.0) + c)
+        score[l] = _F32(c * _F32(_F32(1.0) + sc[l, i]))
+    C = [l for l in U if score[l] >= _F32(theta)]
+    if not C and U:
+        C = [_best([score[l] for l in U], U)]
+    out = np.zeros(L, dtype=bool)
+    out[C] = True
+    return out, st, sc, score
+
+
+# --------------------------------------------------------------------------------------------
+# The whole step
+# --------------------------------------------------------------------------------------------
+def _policy_fields(p) -> tuple:
+    if isinstance(p, dict):
+        return int(p["kind"]), float(p["threshold"]), float(p.get("decay", 0.0)), int(p.get("max_depth", 0))
+    if hasattr(p, "kind"):
+        return int(p.kind), float(p.threshold), float(getattr(p, "decay", 0.0)), int(getattr(p, "max_depth", 0))
+    kind, thr, dec, depth = p
+    return int(kind), float(thr), float(dec), int(depth)
+
+
+def decode_step(hidden: np.ndarray, W: np.ndarray, mask: np.ndarray, policies: Iterable,
+                credit_tok: np.ndarray | None = None, credit_val: np.ndarray | None = None,
+                auto_advance: bool = False, stats: dict | None = None) -> dict:
+    """One decode step over ``B`` sequences of ``L`` positions.
+
+    ``hidden`` ``[B][L][H]``, ``W`` ``[V][H]`` (uint16 bf16 bits or float32),
+    ``mask`` ``[B][L]`` (non-zero = still masked), one policy per sequence
+    (``(kind, threshold, decay, max_depth)``, a dict or an object with those
+    fields), credit state ``[B][L][SLOTS]`` (token, credit) when any policy is
+    credit decoding.  With ``auto_advance`` a sequence whose mask is empty on
+    entry starts a new block first (mask refilled, credit cleared), as the
+    iteration manager moves to the next fixed-size block.  ``stats`` may pass
+    precomputed :func:`token_stats` output.
+
+    Returns new arrays: ``tokens`` (candidate of every row, R17), ``commit``,
+    ``mask``, ``credit_tok``, ``credit_val``, ``conf``, ``gap``, ``score``.
+    """
+    hidden = np.asarray(hidden)
+    B, L = hidden.shape[0], hidden.shape[1]
+    policies = [_policy_fields(p) for p in policies]
+    assert len(policies) == B
+    st = token_stats(hidden, W) if stats is None else stats
+    conf, tok, gap = st["conf"].reshape(B, L), st["tok"].reshape(B, L), st["gap"].reshape(B, L)
+    new_mask = (np.asarray(mask).reshape(B, L) != 0).copy()
+    if credit_tok is None:
+        ctok = np.full((B, L, SLOTS), EMPTY, dtype=np.int32)
+        cval = np.zeros((B, L, SLOTS), dtype=np.float32)
+    else:
+        ctok = np.array(credit_tok, dtype=np.int32, copy=True).reshape(B, L, SLOTS)
+        cval = np.array(credit_val, dtype=np.float32, copy=True).reshape(B, L, SLOTS)
+    commit = np.zeros((B, L), dtype=bool)
+    score = np.full((B, L), -np.inf, dtype=np.float32)
+    for b, (kind, thr, dec, depth) in enumerate(policies):
+        if auto_advance and not new_mask[b].any():
+            new_mask[b] = True
+            ctok[b] = EMPTY
+            cval[b] = 0.0
+        if kind == THRESHOLD:
+            commit[b] = commit_threshold(conf[b], new_mask[b], thr)
+        elif kind == HIERARCHICAL:
+            commit[b] = commit_hierarchical(conf[b], new_mask[b], thr, depth)
+        elif kind == CREDIT:
+            commit[b], ctok[b], cval[b], score[b] = commit_credit(
+                conf[b], tok[b], new_mask[b], ctok[b], cval[b], dec, thr)
+        else:
+            raise ValueError(f"unknown policy kind {kind}")
+        new_mask[b] &= ~commit[b]
+    return {
+        "tokens": tok.astype(np.int32),
+        "commit": commit.astype(np.uint8),
+        "mask": new_mask.astype(np.uint8),
+        "credit_tok": ctok,
+        "credit_val": cval,
+        "conf": conf.astype(np.float32),
+        "gap": gap.astype(np.float32),
+        "score": score,
+    }
