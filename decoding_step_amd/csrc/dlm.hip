@@ -1,0 +1,269 @@
+// Host side of the C ABI declared in include/dlm.h: argument validation (before any HIP call),
+// launch planning, workspace layout and the launches themselves.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <algorithm>
+
+#include "dlm.h"
+#include "dlm_device.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return DLM_OK;
+}
+
+constexpr size_t kTicketBytes = 256;     // completion counter, padded to a cache line
+constexpr size_t kLdsBudget = 160 * 1024;  // gfx950 LDS per workgroup
+constexpr int kTargetWorkgroups = 256;   // one per compute unit on MI355X
+
+// Launch geometry of one step, a pure function of the shapes (so the workspace size is too).
+struct Plan {
+  int MR = 0;        // hidden rows per workgroup (16 or 32)
+  int n_rg = 0;      // row groups
+  int G_v = 0;       // vocabulary ranges, multiple of 8
+  int ntiles = 0;    // 16-row vocabulary tiles
+  size_t lds = 0;    // dynamic LDS bytes
+  size_t ws = 0;     // workspace bytes
+};
+
+int elem_bytes(int32_t dtype) { return dtype == DLM_BF16 ? 2 : dtype == DLM_F32 ? 4 : 0; }
+
+int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p) {
+  const int es = elem_bytes(dtype);
+  if (!es) return fail(DLM_ERR_DTYPE, "dtype %d is neither DLM_F32 (0) nor DLM_BF16 (1)", (int)dtype);
+  if (B < 1 || B > DLM_MAX_SEQS) return fail(DLM_ERR_SHAPE, "B=%lld outside [1, %d]", (long long)B, DLM_MAX_SEQS);
+  if (L < 1 || L > DLM_MAX_L) return fail(DLM_ERR_SHAPE, "L=%lld outside [1, %d]", (long long)L, DLM_MAX_L);
+  if (H < 32 || H % 32) return fail(DLM_ERR_SHAPE, "H=%lld must be a positive multiple of 32", (long long)H);
+  if (V < 1) return fail(DLM_ERR_SHAPE, "V=%lld must be >= 1", (long long)V);
+  const int64_t M = B * L;
+  const int64_t ntiles = (V + dlm::kTileRows - 1) / dlm::kTileRows;
+  if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
+  int MR = M > 16 ? 32 : 16;
+  auto lds_for = [&](int mr) { return dlm::lds_bytes((size_t)mr * H * es / 16, mr); };
+  if (lds_for(MR) > kLdsBudget) MR = 16;
+  if (lds_for(MR) > kLdsBudget)
+    return fail(DLM_ERR_SHAPE, "H=%lld too large: 16 hidden rows need %zu bytes of LDS (limit %zu)",
+                (long long)H, lds_for(MR), kLdsBudget);
+  const int n_rg = (int)((M + MR - 1) / MR);
+  int G_v = (kTargetWorkgroups / n_rg) / 8 * 8;
+  if (G_v < 8) G_v = 8;
+  const int64_t need = ((ntiles + dlm::kWaves - 1) / dlm::kWaves + 7) / 8 * 8;  // >= 1 tile per wave
+  if (G_v > need) G_v = (int)need;
+  if (G_v > dlm::kMaxVocabGroups) G_v = dlm::kMaxVocabGroups;
+  // each workgroup's W range must stay addressable by a 31-bit buffer offset
+  const int64_t range_bytes = ((ntiles + G_v - 1) / G_v) * dlm::kTileRows * H * es;
+  if (range_bytes >= (1ll << 31) - 64)
+    return fail(DLM_ERR_SHAPE, "V*H too large: %lld bytes of W per workgroup", (long long)range_bytes);
+  if ((int64_t)n_rg * G_v > (1ll << 30)) return fail(DLM_ERR_SHAPE, "too many rows");
+  p->MR = MR;
+  p->n_rg = n_rg;
+  p->G_v = G_v;
+  p->ntiles = (int)ntiles;
+  p->lds = lds_for(MR);
+  p->ws = kTicketBytes + (size_t)n_rg * G_v * MR * 16;
+  return DLM_OK;
+}
+
+bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+// Validate the per-sequence rules and pack them (distinct rules + index per sequence).
+int pack_rules(const dlm_policy* pol, bool need_credit_state, const void* credit, dlm::CommitArgs* c) {
+  if (!pol->seq) return fail(DLM_ERR_NULL, "policy->seq is NULL");
+  int n = 0;
+  bool any_credit = false;
+  for (int64_t b = 0; b < pol->B; ++b) {
+    const dlm_seq_policy& s = pol->seq[b];
+    if (s.kind != DLM_THRESHOLD && s.kind != DLM_HIERARCHICAL && s.kind != DLM_CREDIT)
+      return fail(DLM_ERR_POLICY, "seq[%lld].kind=%d is not a known policy", (long long)b, (int)s.kind);
+    if (!std::isfinite(s.threshold))
+      return fail(DLM_ERR_POLICY, "seq[%lld].threshold is not finite", (long long)b);
+    if (s.kind == DLM_CREDIT && !(s.decay >= 0.f && s.decay < 1.f))
+      return fail(DLM_ERR_POLICY, "seq[%lld].decay=%g outside [0, 1)", (long long)b, (double)s.decay);
+    if (s.kind == DLM_HIERARCHICAL && s.max_depth < 0)
+      return fail(DLM_ERR_POLICY, "seq[%lld].max_depth=%d is negative", (long long)b, (int)s.max_depth);
+    any_credit |= s.kind == DLM_CREDIT;
+    dlm::Rule r;
+    r.kind = s.kind;
+    r.thr = s.threshold;
+    r.decay = s.kind == DLM_CREDIT ? s.decay : 0.f;
+    r.depth = s.kind == DLM_HIERARCHICAL ? s.max_depth : 0;
+    int k = 0;
+    for (; k < n; ++k)
+      if (std::memcmp(&c->rules[k], &r, sizeof r) == 0) break;
+    if (k == n) {
+      if (n == DLM_MAX_RULES)
+        return fail(DLM_ERR_POLICY, "more than %d distinct per-sequence rules in one call", DLM_MAX_RULES);
+      c->rules[n++] = r;
+    }
+    c->rule_of[b] = (uint8_t)k;
+  }
+  if (need_credit_state && any_credit && !credit)
+    return fail(DLM_ERR_NULL, "credit_state is NULL but a sequence uses DLM_CREDIT");
+  return DLM_OK;
+}
+
+template <class T, int MR>
+int launch_step(const dlm::StepArgs& a, const Plan& p, hipStream_t stream) {
+  // Raise the kernel's dynamic-LDS limit once per device (idempotent; a race only repeats it).
+  static std::atomic<uint64_t> attr_set{0};
+  auto kern = dlm::step_kernel<T, MR>;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(DLM_ERR_HIP, "hipGetDevice failed");
+  }
+  const uint64_t bit = 1ull << (dev & 63);
+  if (!(attr_set.load(std::memory_order_relaxed) & bit)) {
+    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsBudget) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(DLM_ERR_HIP, "hipFuncSetAttribute(max dynamic LDS = %zu) failed", kLdsBudget);
+    }
+    attr_set.fetch_or(bit, std::memory_order_relaxed);
+  }
+  hipLaunchKernelGGL(kern, dim3(p.n_rg * p.G_v), dim3(dlm::kThreads), p.lds, stream, a);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DLM_ERR_HIP, "step kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::CommitArgs c, bool commit) {
+  Plan p;
+  int rc = make_plan(pol->B, pol->L, pol->H, pol->V, pol->dtype, &p);
+  if (rc) return rc;
+  if (!pol->workspace) return fail(DLM_ERR_NULL, "policy->workspace is NULL");
+  if (pol->workspace_bytes < p.ws)
+    return fail(DLM_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", pol->workspace_bytes, p.ws);
+  if (misaligned(hidden, 16) || misaligned(W, 16) || misaligned(pol->workspace, 256))
+    return fail(DLM_ERR_SHAPE, "hidden and W_vocab must be 16-byte aligned, the workspace 256-byte aligned");
+  dlm::StepArgs a;
+  a.hidden = hidden;
+  a.W = W;
+  a.ticket = static_cast<unsigned*>(pol->workspace);
+  a.partials = reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + kTicketBytes);
+  a.H = (int)pol->H;
+  a.V = (int)pol->V;
+  a.M = (int)(pol->B * pol->L);
+  a.n_rg = p.n_rg;
+  a.G_v = p.G_v;
+  a.ntiles = p.ntiles;
+  c.B = (int)pol->B;
+  c.L = (int)pol->L;
+  c.flags = (commit ? dlm::kFlagCommit : 0u) | (commit ? (pol->flags & DLM_AUTO_ADVANCE) : 0u);
+  a.c = c;
+  hipStream_t stream = static_cast<hipStream_t>(pol->stream);
+  if (pol->dtype == DLM_BF16)
+    return p.MR == 32 ? launch_step<uint16_t, 32>(a, p, stream) : launch_step<uint16_t, 16>(a, p, stream);
+  return p.MR == 32 ? launch_step<float, 32>(a, p, stream) : launch_step<float, 16>(a, p, stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state, dlm_credit_slot* credit_state,
+                    const dlm_policy* policy, int32_t* out_tokens, uint8_t* out_commit) {
+  if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");
+  if (!hidden || !W_vocab || !mask_state || !out_tokens || !out_commit)
+    return fail(DLM_ERR_NULL, "hidden, W_vocab, mask_state, out_tokens and out_commit must be non-NULL");
+  dlm::CommitArgs c;
+  std::memset(&c, 0, sizeof c);
+  Plan p;
+  int rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, &p);
+  if (rc) return rc;
+  rc = pack_rules(policy, true, credit_state, &c);
+  if (rc) return rc;
+  c.mask = mask_state;
+  c.credit = credit_state;
+  c.out_tokens = out_tokens;
+  c.out_commit = out_commit;
+  c.out_conf = policy->out_conf;
+  c.out_gap = policy->out_gap;
+  return run_step(hidden, W_vocab, policy, c, true);
+}
+
+int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* policy, float* out_conf,
+                    int32_t* out_tokens, float* out_gap) {
+  if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");
+  if (!hidden || !W_vocab || !out_conf || !out_tokens)
+    return fail(DLM_ERR_NULL, "hidden, W_vocab, out_conf and out_tokens must be non-NULL");
+  dlm::CommitArgs c;
+  std::memset(&c, 0, sizeof c);
+  c.out_tokens = out_tokens;
+  c.out_conf = out_conf;
+  c.out_gap = out_gap;
+  return run_step(hidden, W_vocab, policy, c, false);
+}
+
+int dlm_commit(const float* conf, const int32_t* tokens, uint8_t* mask_state, dlm_credit_slot* credit_state,
+               const dlm_policy* policy, uint8_t* out_commit) {
+  if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");
+  if (!conf || !tokens || !mask_state || !out_commit)
+    return fail(DLM_ERR_NULL, "conf, tokens, mask_state and out_commit must be non-NULL");
+  if (policy->B < 1 || policy->B > DLM_MAX_SEQS)
+    return fail(DLM_ERR_SHAPE, "B=%lld outside [1, %d]", (long long)policy->B, DLM_MAX_SEQS);
+  if (policy->L < 1 || policy->L > DLM_MAX_L)
+    return fail(DLM_ERR_SHAPE, "L=%lld outside [1, %d]", (long long)policy->L, DLM_MAX_L);
+  dlm::CommitArgs c;
+  std::memset(&c, 0, sizeof c);
+  int rc = pack_rules(policy, true, credit_state, &c);
+  if (rc) return rc;
+  c.mask = mask_state;
+  c.credit = credit_state;
+  c.out_tokens = nullptr;  // the candidates are the caller's input here
+  c.out_commit = out_commit;
+  c.B = (int)policy->B;
+  c.L = (int)policy->L;
+  c.flags = policy->flags & DLM_AUTO_ADVANCE;
+  const int grid = (c.B + dlm::kWaves - 1) / dlm::kWaves;
+  hipLaunchKernelGGL(dlm::commit_kernel, dim3(grid), dim3(dlm::kThreads), 0, static_cast<hipStream_t>(policy->stream),
+                     c, conf, tokens);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DLM_ERR_HIP, "commit kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+size_t dlm_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype) {
+  Plan p;
+  const std::string saved = g_last_error;
+  const int rc = make_plan(B, L, H, V, dtype, &p);
+  g_last_error = saved;
+  return rc ? 0 : p.ws;
+}
+
+int dlm_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  if (!workspace) return fail(DLM_ERR_NULL, "workspace is NULL");
+  if (workspace_bytes == 0) return ok();
+  const size_t blocks = std::min<size_t>(1024, (workspace_bytes + 16 * 256 - 1) / (16 * 256));
+  hipLaunchKernelGGL(dlm::fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint8_t*>(workspace), workspace_bytes);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DLM_ERR_HIP, "fill kernel launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* dlm_last_error(void) { return g_last_error.c_str(); }
+
+const char* dlm_version(void) { return DLM_VERSION_STRING; }
+
+}  // extern "C"

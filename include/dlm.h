@@ -1,0 +1,155 @@
+/*
+ * dlm.h -- C ABI of the per-iteration parallel-decoding step of a masked
+ * diffusion language model, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources.  The step follows the dInfer explainer (91haoming.cn, a summary of
+ * arXiv 2510.08666):
+ *   - decoding-strategy component: positions are fixed by the model's
+ *     confidence in each position's text, with three strategies -- threshold
+ *     decoding, hierarchical decoding (split the regions still to fill
+ *     recursively and fix region centres first) and credit decoding (a credit
+ *     per position and candidate, accumulated across iterations);
+ *   - diffusion-iteration manager: fixed-size blocks are handled in turn;
+ *     a block of L positions is the unit of one step.
+ * One step = LM head z = h W^T over every row of the block, per-row candidate
+ * (arg-max, lowest id on ties) and confidence (largest softmax probability),
+ * then the sequence's commit policy, with at least one commit per step while
+ * a position is still masked.
+ *
+ * Conventions for every entry point.
+ *   - Tensors are dense, row-major, caller-owned DEVICE memory unless stated.
+ *   - All work is enqueued on `stream` (a hipStream_t; NULL = null stream);
+ *     calls are asynchronous: errors found while the kernels run surface on
+ *     the stream, HIP-style.
+ *   - Arguments are validated on the host BEFORE any HIP call; on a non-zero
+ *     status nothing is enqueued and nothing is written.  dlm_last_error()
+ *     then returns a message (thread-local).
+ *   - The library never allocates device memory in these calls and keeps no
+ *     mutable global state; calls on different streams must use different
+ *     workspaces.
+ */
+#ifndef DLM_H
+#define DLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DLM_VERSION_STRING "0.1.0"
+
+#define DLM_MAX_SEQS 256   /* sequences per call                                  */
+#define DLM_MAX_L 64       /* positions per block: one wavefront lane per position */
+#define DLM_CREDIT_SLOTS 4 /* tracked (token, credit) candidates per position      */
+#define DLM_MAX_RULES 8    /* distinct dlm_seq_policy values per call              */
+
+/* Status codes. */
+enum {
+  DLM_OK = 0,
+  DLM_ERR_NULL = -1,      /* a required pointer is NULL                              */
+  DLM_ERR_DTYPE = -2,     /* dtype is not DLM_F32 / DLM_BF16                         */
+  DLM_ERR_SHAPE = -3,     /* B, L, H or V outside the supported range                */
+  DLM_ERR_POLICY = -4,    /* bad policy kind / parameter, or too many distinct rules */
+  DLM_ERR_WORKSPACE = -5, /* workspace smaller than dlm_workspace_bytes()            */
+  DLM_ERR_HIP = -6        /* the HIP runtime refused a launch                        */
+};
+
+/* Element type of hidden and W_vocab (both the same). */
+enum { DLM_F32 = 0, DLM_BF16 = 1 };
+
+/* Commit strategies (explainer, decoding-strategy component). */
+enum { DLM_THRESHOLD = 0, DLM_HIERARCHICAL = 1, DLM_CREDIT = 2 };
+
+/* dlm_policy.flags */
+enum {
+  /* A sequence whose mask is empty on entry starts its next block first: the
+   * mask row is refilled with ones and its credit slots are cleared (explainer,
+   * diffusion-iteration manager: fixed-size blocks in turn).  Without it such a
+   * sequence commits nothing and nothing of it changes except out_tokens. */
+  DLM_AUTO_ADVANCE = 1u
+};
+
+/* One tracked candidate of a position; token -1 marks an empty slot (credit 0). */
+typedef struct {
+  int32_t token;
+  float credit;
+} dlm_credit_slot;
+
+/* The rule one sequence is decoded with. */
+typedef struct {
+  int32_t kind;      /* DLM_THRESHOLD / DLM_HIERARCHICAL / DLM_CREDIT                     */
+  float threshold;   /* threshold, hierarchical: tau on conf; credit: theta on score     */
+  float decay;       /* credit only: per-iteration credit factor, 0 <= decay < 1          */
+  int32_t max_depth; /* hierarchical only: split depth limit, 0 = unbounded (runs = 1)    */
+} dlm_seq_policy;
+
+/* Shapes, per-sequence rules and launch context of one call. */
+typedef struct {
+  int64_t B;                 /* sequences, 1..DLM_MAX_SEQS                                 */
+  int64_t L;                 /* positions per block, 1..DLM_MAX_L                          */
+  int64_t H;                 /* hidden size, multiple of 32 (limits: see dlm_workspace_bytes) */
+  int64_t V;                 /* vocabulary size, >= 1                                      */
+  int32_t dtype;             /* DLM_F32 or DLM_BF16                                        */
+  uint32_t flags;            /* DLM_AUTO_ADVANCE                                           */
+  const dlm_seq_policy* seq; /* HOST array [B]; at most DLM_MAX_RULES distinct entries     */
+  void* workspace;           /* device scratch, >= dlm_workspace_bytes(B, L, H, V, dtype)   */
+  size_t workspace_bytes;    /* its size; must be zero-filled before its first use         */
+  void* stream;              /* hipStream_t                                                */
+  float* out_conf;           /* optional device [B][L]: confidence of every row, or NULL   */
+  float* out_gap;            /* optional device [B][L]: top-1 minus top-2 logit, or NULL   */
+} dlm_policy;
+
+/*
+ * One decode step.
+ *   hidden       [B][L][H]   dtype    block hidden states (row b*L + l)
+ *   W_vocab      [V][H]      dtype    vocabulary head
+ *   mask_state   [B][L]      uint8    in/out: 1 = still masked; only 1 -> 0 changes
+ *                                     (plus the refill of DLM_AUTO_ADVANCE)
+ *   credit_state [B][L][4]   slots    in/out; only rows masked on entry change.
+ *                                     May be NULL iff no sequence uses DLM_CREDIT.
+ *   policy                            shapes, rules, workspace, stream, diagnostics
+ *   out_tokens   [B][L]      int32    candidate (arg-max token) of EVERY row
+ *   out_commit   [B][L]      uint8    1 where this call fixed the position
+ * Every row goes through the LM head; the [B][L][V] logits never reach memory.
+ * The workspace carries a completion counter that each call leaves at zero.
+ */
+int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state,
+                    dlm_credit_slot* credit_state, const dlm_policy* policy, int32_t* out_tokens,
+                    uint8_t* out_commit);
+
+/*
+ * LM head + per-row statistics only (no commit): for every row, the
+ * confidence, the candidate token and the top-2 logit gap.  policy->seq,
+ * flags, out_conf and out_gap are ignored; out_gap may be NULL.
+ */
+int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* policy,
+                    float* out_conf, int32_t* out_tokens, float* out_gap);
+
+/*
+ * Commit policies only, from given per-row confidences and candidates
+ * (conf [B][L] float, tokens [B][L] int32, device).  Same state semantics as
+ * dlm_decode_step; out_tokens of that call equals `tokens` here.  policy->H,
+ * V, dtype, workspace, out_conf and out_gap are ignored.
+ */
+int dlm_commit(const float* conf, const int32_t* tokens, uint8_t* mask_state,
+               dlm_credit_slot* credit_state, const dlm_policy* policy, uint8_t* out_commit);
+
+/* Workspace bytes a call with these shapes needs (0 if the shapes are unsupported). */
+size_t dlm_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype);
+
+/* Zero-fill a workspace on `stream` (a fill kernel, safe under graph capture). */
+int dlm_workspace_init(void* workspace, size_t workspace_bytes, void* stream);
+
+/* Message of the last non-zero status on this thread ("" if none). */
+const char* dlm_last_error(void);
+
+/* Library version, DLM_VERSION_STRING. */
+const char* dlm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLM_H */

@@ -9,15 +9,15 @@ What one step computes, and where it comes from.  The pages are four news
 pages about dInfer; the mechanisms are only on the Traditional-Chinese
 explainer of arXiv 2510.08666 hosted on 91haoming.cn ("the explainer"):
 
-* the decoding-strategy component of the explainer fixes a position's
-  token "according to the AI's confidence in the text at each position":
-  this presupposes, per position, a candidate token and a confidence.  The
+* the decoding-strategy component of the explainer decides whether to fix
+  a position from how sure the model is about that position's text, which
+  presupposes, per position, a candidate token and a confidence.  The
   candidate is the arg-max of the logits ``z = h W^T`` of the vocabulary
   head, the confidence the largest softmax probability ``1 / sum_v
   exp(z_v - max z)``;
 * threshold decoding (same component, first strategy): fix at once every
-  masked position whose confidence is high enough, keep "thinking" about
-  the others;
+  masked position whose confidence is high enough and leave the others
+  for later iterations;
 * hierarchical decoding (second strategy): split the regions still to be
   filled recursively into sub-regions and fix the centre of each region
   first;
@@ -72,10 +72,12 @@ _F32 = np.float32
 def as_f64(x: np.ndarray) -> np.ndarray:
     """Exact float64 values of float32 data or of bfloat16 bit patterns (uint16)."""
     x = np.asarray(x)
+    if x.dtype == np.float64:
+        return x                      # already widened (lets callers widen a large W once)
     if x.dtype == np.uint16:
         # a bfloat16 value is the float32 whose upper half is the pattern
         return (x.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    if x.dtype == np.float32 or x.dtype == np.float64:
+    if x.dtype == np.float32:
         return x.astype(np.float64)
     raise TypeError(f"unsupported input dtype {x.dtype}")
 

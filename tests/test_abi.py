@@ -1,0 +1,160 @@
+"""The C ABI without a GPU: exports, sizing, and every host-side validation error.
+
+Validation happens before any HIP call, so these calls pass fake (non-NULL,
+never dereferenced) device addresses and expect the documented status.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from decoding_step_amd import _native as nat
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dlm.h")
+FAKE = 0x10000          # 256-byte aligned, never dereferenced
+MISALIGNED = 0x10008
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return nat.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(dlm_[a-z_]+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert set(names) >= {"dlm_decode_step", "dlm_token_stats", "dlm_commit", "dlm_workspace_bytes",
+                          "dlm_workspace_init", "dlm_last_error", "dlm_version"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_matches_header(lib):
+    m = re.search(r'#define DLM_VERSION_STRING "([^"]+)"', open(HEADER).read())
+    assert nat.dlm_version() == m.group(1)
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ["DLM_MAX_SEQS", "DLM_MAX_L", "DLM_CREDIT_SLOTS", "DLM_MAX_RULES"]:
+        assert int(re.search(rf"#define {name} (\d+)", text).group(1)) == getattr(nat, name)
+    assert ctypes.sizeof(nat.dlm_credit_slot) == 8
+    assert ctypes.sizeof(nat.dlm_seq_policy) == 16
+    assert ctypes.sizeof(nat.dlm_policy) == 88
+
+
+def test_workspace_sizes():
+    # ticket line (256 B) + one 16-byte record per (row group, vocabulary range, row slot)
+    assert nat.dlm_workspace_bytes(1, 32, 2048, 126464, nat.DLM_BF16) == 256 + 1 * 256 * 32 * 16
+    assert nat.dlm_workspace_bytes(1, 64, 2048, 126464, nat.DLM_BF16) == 256 + 2 * 128 * 32 * 16
+    assert nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_F32) == 256 + 1 * 8 * 16 * 16
+    assert nat.dlm_workspace_bytes(16, 32, 2048, 157184, nat.DLM_BF16) > 0
+    for bad in [(0, 8, 64, 64, 0), (1, 65, 64, 64, 0), (1, 8, 48, 64, 0), (1, 8, 64, 0, 0), (1, 8, 64, 64, 5),
+                (257, 8, 64, 64, 1), (1, 8, 1 << 20, 64, 1)]:
+        assert nat.dlm_workspace_bytes(*bad) == 0, bad
+
+
+def policy(B=1, L=8, H=64, V=1024, dtype=nat.DLM_BF16, seq=None, ws=FAKE, ws_bytes=1 << 20, flags=0):
+    seq = seq if seq is not None else [(nat.DLM_THRESHOLD, 0.9, 0.0, 0)] * B
+    return nat.StepPolicy(B, L, H, V, dtype, seq, workspace=ws, workspace_bytes=ws_bytes, flags=flags)
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except nat.DlmError as e:
+        assert nat.dlm_last_error() != ""
+        return e.status
+    return nat.DLM_OK
+
+
+def step(p, hidden=FAKE, W=FAKE, mask=FAKE, credit=FAKE, out_tok=FAKE, out_commit=FAKE):
+    return status_of(nat.dlm_decode_step, hidden, W, mask, credit, p, out_tok, out_commit)
+
+
+def test_null_pointers():
+    p = policy()
+    assert step(p, hidden=None) == nat.DLM_ERR_NULL
+    assert step(p, W=None) == nat.DLM_ERR_NULL
+    assert step(p, mask=None) == nat.DLM_ERR_NULL
+    assert step(p, out_tok=None) == nat.DLM_ERR_NULL
+    assert step(p, out_commit=None) == nat.DLM_ERR_NULL
+    assert nat.load().dlm_decode_step(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE) == nat.DLM_ERR_NULL
+    assert step(policy(ws=None)) == nat.DLM_ERR_NULL
+    assert step(policy(seq=[]), credit=None) == nat.DLM_ERR_NULL           # seq == NULL
+    credit_pol = policy(seq=[(nat.DLM_CREDIT, 1.2, 0.7, 0)])
+    assert step(credit_pol, credit=None) == nat.DLM_ERR_NULL
+
+
+def test_bad_dtype():
+    assert step(policy(dtype=2)) == nat.DLM_ERR_DTYPE
+    assert step(policy(dtype=-1)) == nat.DLM_ERR_DTYPE
+
+
+@pytest.mark.parametrize("kw", [dict(B=0), dict(B=257, seq=[(0, 0.9, 0, 0)] * 257), dict(L=0), dict(L=65),
+                                dict(H=0), dict(H=48), dict(H=16), dict(V=0), dict(H=1 << 16)])
+def test_bad_shapes(kw):
+    assert step(policy(**kw)) == nat.DLM_ERR_SHAPE
+
+
+@pytest.mark.parametrize("seq", [
+    [(7, 0.9, 0.0, 0)],
+    [(-1, 0.9, 0.0, 0)],
+    [(nat.DLM_THRESHOLD, math.nan, 0.0, 0)],
+    [(nat.DLM_THRESHOLD, math.inf, 0.0, 0)],
+    [(nat.DLM_CREDIT, 1.2, 1.0, 0)],
+    [(nat.DLM_CREDIT, 1.2, -0.1, 0)],
+    [(nat.DLM_HIERARCHICAL, 0.7, 0.0, -1)],
+])
+def test_bad_policies(seq):
+    assert step(policy(seq=seq)) == nat.DLM_ERR_POLICY
+
+
+def test_too_many_distinct_rules():
+    seq = [(nat.DLM_THRESHOLD, 0.5 + 0.01 * i, 0.0, 0) for i in range(9)]
+    assert step(policy(B=9, seq=seq)) == nat.DLM_ERR_POLICY
+    seq = [(nat.DLM_THRESHOLD, 0.5 + 0.01 * (i % 8), 0.0, 0) for i in range(200)]
+    # 8 distinct rules over 200 sequences pass validation; a tiny workspace then stops the call
+    assert step(policy(B=200, seq=seq, ws_bytes=16)) == nat.DLM_ERR_WORKSPACE
+
+
+def test_workspace_too_small():
+    need = nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_BF16)
+    assert step(policy(ws_bytes=need - 1)) == nat.DLM_ERR_WORKSPACE
+
+
+def test_misaligned_pointers():
+    need = nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_BF16)
+    assert step(policy(ws_bytes=need), hidden=MISALIGNED) == nat.DLM_ERR_SHAPE
+    assert step(policy(ws_bytes=need), W=MISALIGNED) == nat.DLM_ERR_SHAPE
+    assert step(policy(ws=MISALIGNED, ws_bytes=need)) == nat.DLM_ERR_SHAPE
+
+
+def test_token_stats_and_commit_validation():
+    p = policy()
+    assert status_of(nat.dlm_token_stats, None, FAKE, p, FAKE, FAKE) == nat.DLM_ERR_NULL
+    assert status_of(nat.dlm_token_stats, FAKE, FAKE, p, None, FAKE) == nat.DLM_ERR_NULL
+    assert status_of(nat.dlm_token_stats, FAKE, FAKE, policy(L=100), FAKE, FAKE) == nat.DLM_ERR_SHAPE
+    assert status_of(nat.dlm_commit, None, FAKE, FAKE, FAKE, p, FAKE) == nat.DLM_ERR_NULL
+    assert status_of(nat.dlm_commit, FAKE, FAKE, FAKE, FAKE, policy(L=65), FAKE) == nat.DLM_ERR_SHAPE
+    assert status_of(nat.dlm_commit, FAKE, FAKE, FAKE, FAKE, policy(seq=[(9, 0.9, 0, 0)]), FAKE) == nat.DLM_ERR_POLICY
+    assert status_of(nat.dlm_commit, FAKE, FAKE, FAKE, None, policy(seq=[(2, 1.2, 0.7, 0)]), FAKE) == nat.DLM_ERR_NULL
+    assert status_of(nat.dlm_workspace_init, None, 16) == nat.DLM_ERR_NULL
+
+
+def test_binding_raises_without_library(tmp_path):
+    saved = nat._lib
+    try:
+        nat._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            nat.load(str(tmp_path / "missing.so"))
+    finally:
+        nat._lib = saved
