@@ -1,0 +1,203 @@
+#!/usr/bin/env python3
+"""Decode-step throughput on one MI355X: positions/s of dlm_decode_step.
+
+One step = LM head over every row of the block + confidence/candidate +
+commit policy + state update: one launch of the fused kernel.  The
+default workload is B=1, L=32, H=2048, V=126464, bf16, threshold 0.9.
+
+Inputs are seeded and synthetic and already resident in HBM when the timed
+region starts.  An untimed pass first records the trajectory: which
+(block, iteration) each sequence sits at, step by step, with automatic
+block advance.  The timed pass replays the same inputs from the same
+initial state.  The kernels are deterministic, so it follows the same
+trajectory without a host round trip between steps.
+
+Prints ONE JSON line (rank 0).  Extra keys: ``roofline`` for the step kernel
+(algorithmic bytes / measured time, against 8 TB/s HBM or 2.5 PFLOP/s
+bf16 MFMA) and ``cpu_baseline`` (the CPU oracle on a bounded sample).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # dense bf16
+MFMA_FP32_PEAK_TFLOPS = 157.3
+METRIC = "decode-step positions/sec (LM head+confidence+commit), B=1 L=32; % HBM/MFMA peak"
+
+
+def algorithmic_work(wl):
+    """Bytes the step must move and flops it must do (the [M][V] logits are never stored)."""
+    es = 2 if wl.dtype == "bf16" else 4
+    M = wl.B * wl.L
+    any_credit = any(p.kind == 2 for p in wl.policies)
+    state = M * (1 + 1 + 4 + 1 + 4 + 4)            # mask in/out, tokens, commit, conf, gap
+    if any_credit:
+        state += 2 * M * 4 * 8                     # credit slots in/out
+    bytes_ = wl.V * wl.H * es + M * wl.H * es + state
+    flops = 2.0 * M * wl.V * wl.H
+    return bytes_, flops
+
+
+def record_trajectory(wl, W, Wd, steps, dev):
+    """Untimed: step once per input with host sync, recording the inputs each step consumed."""
+    import numpy as np
+    import torch
+    from decoding_step_amd import _native as nat
+    from decoding_step_amd.device import Decoder, new_credit, to_device
+    from decoding_step_amd.synth import BlockStream
+
+    seq = [(p.kind, p.threshold, p.decay, p.max_depth) for p in wl.policies]
+    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE)
+    streams = [BlockStream(W, wl.L, s, wl.a_max, rp) for s, rp in zip(wl.seeds, wl.redraw_p)]
+    pos = [[0, 0] for _ in range(wl.B)]
+    mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
+    credit = new_credit(wl.B, wl.L, dev)
+    hidden = torch.empty((steps, wl.B, wl.L, wl.H), dtype=Wd.dtype, device=dev)
+    commits = 0
+    for s in range(steps):
+        h = np.stack([streams[b].hidden(*pos[b]) for b in range(wl.B)])
+        hidden[s].copy_(to_device(h, dev))
+        dec.step(hidden[s], mask, credit)
+        m = mask.cpu().numpy()
+        commits += int(dec.out_commit.sum().item())
+        for b in range(wl.B):
+            pos[b] = [pos[b][0] + 1, 0] if not m[b].any() else [pos[b][0], pos[b][1] + 1]
+    blocks_done = sum(p[0] for p in pos)
+    return hidden, seq, commits, blocks_done
+
+
+def time_steps(wl, Wd, hidden, seq, warmup, steps, dev):
+    import torch
+    from decoding_step_amd import _native as nat
+    from decoding_step_amd.device import Decoder, new_credit
+
+    stream = torch.cuda.current_stream(dev)
+    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream)
+    mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
+    credit = new_credit(wl.B, wl.L, dev)
+    for s in range(warmup):                      # warm-up on the first inputs, then reset the state
+        dec.step(hidden[s % hidden.shape[0]], mask, credit)
+    torch.cuda.synchronize()
+    mask.fill_(1)
+    credit.copy_(new_credit(wl.B, wl.L, dev))
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    for s in range(steps):
+        dec.step(hidden[s], mask, credit)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / 1e3, wall
+
+
+def cpu_baseline(wl, W, budget_s=20.0):
+    """The oracle as it stands, on the first steps of the same workload, on this host's cores."""
+    import numpy as np
+    import oracle
+    from decoding_step_amd.synth import BlockStream
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    seq = [(p.kind, p.threshold, p.decay, p.max_depth) for p in wl.policies]
+    streams = [BlockStream(W, wl.L, s, wl.a_max, rp) for s, rp in zip(wl.seeds, wl.redraw_p)]
+    mask = np.ones((wl.B, wl.L), np.uint8)
+    ctok = np.full((wl.B, wl.L, 4), -1, np.int32)
+    cval = np.zeros((wl.B, wl.L, 4), np.float32)
+    pos = [[0, 0] for _ in range(wl.B)]
+    n, t = 0, 0.0
+    while t < budget_s and n < 64:
+        h = np.stack([streams[b].hidden(*pos[b]) for b in range(wl.B)])
+        t0 = time.perf_counter()
+        out = oracle.decode_step(h, W, mask, seq, ctok, cval, auto_advance=True)
+        t += time.perf_counter() - t0
+        mask, ctok, cval = out["mask"], out["credit_tok"], out["credit_val"]
+        for b in range(wl.B):
+            pos[b] = [pos[b][0] + 1, 0] if not mask[b].any() else [pos[b][0], pos[b][1] + 1]
+        n += 1
+    return {"value": wl.B * wl.L * n / t, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} steps of {wl.name} (whole steps, all {wl.B * wl.L} rows), {t:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="threshold_b1_l32")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the step shards by sequence or by vocabulary range; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from decoding_step_amd import _native as nat
+    from decoding_step_amd.device import to_device
+    from decoding_step_amd.synth import make_weights
+    from decoding_step_amd.workloads import WORKLOADS
+
+    nat.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = WORKLOADS[args.workload]
+    print(f"[bench] workload {wl.name}: generating W ({wl.V}x{wl.H} {wl.dtype})", file=sys.stderr, flush=True)
+    W = make_weights(wl.V, wl.H, wl.dtype)
+    Wd = to_device(W, dev)
+    n_in = max(args.steps, 1)
+    print(f"[bench] recording {n_in} steps", file=sys.stderr, flush=True)
+    hidden, seq, commits, blocks = record_trajectory(wl, W, Wd, n_in, dev)
+    print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
+    t, wall = time_steps(wl, Wd, hidden, seq, args.warmup, args.steps, dev)
+    ms = t / args.steps * 1e3
+    bytes_, flops = algorithmic_work(wl)
+    sec_per_step = t / args.steps
+    if flops / bytes_ > 312 and wl.dtype == "bf16":
+        roof = {"bound": "mfma", "achieved": flops / sec_per_step / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": bytes_ / sec_per_step / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = "dlm::step_kernel (one launch per step)"
+    roof["algorithmic_bytes_per_launch"] = bytes_
+    roof["algorithmic_flops_per_launch"] = flops
+    out = {
+        "metric": METRIC, "value": wl.B * wl.L / sec_per_step, "unit": "positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": wl.dtype,
+        "data": "synthetic (seeded generator: W ~ N(0,0.02), planted-peak hidden states)",
+        "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "H": wl.H, "V": wl.V,
+                   "policies": sorted(set(f"{['threshold', 'hierarchical', 'credit'][p.kind]} {p.threshold}"
+                                          for p in wl.policies))},
+        "roofline": roof,
+        "committed_tok_per_s": commits / args.steps / sec_per_step,
+        "blocks_completed": blocks,
+        "host_wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(wl, W, args.cpu_budget)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

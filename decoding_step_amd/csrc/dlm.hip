@@ -2,7 +2,6 @@
 // launch planning, workspace layout and the launches themselves.
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -33,12 +32,12 @@ int ok() {
 }
 
 constexpr size_t kTicketBytes = 256;     // completion counter, padded to a cache line
-constexpr size_t kLdsBudget = 160 * 1024;  // gfx950 LDS per workgroup
 constexpr int kTargetWorkgroups = 256;   // one per compute unit on MI355X
 
 // Launch geometry of one step, a pure function of the shapes (so the workspace size is too).
 struct Plan {
-  int MR = 0;        // hidden rows per workgroup (16 or 32)
+  int NMB = 0;       // 16-row blocks of hidden rows per workgroup (1, 2 or 4)
+  int KFWM = 0;      // K fragments per wavefront per tile, rounded up (2, 8 or 16)
   int n_rg = 0;      // row groups
   int G_v = 0;       // vocabulary ranges, multiple of 8
   int ntiles = 0;    // 16-row vocabulary tiles
@@ -58,29 +57,34 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
   const int64_t M = B * L;
   const int64_t ntiles = (V + dlm::kTileRows - 1) / dlm::kTileRows;
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
-  int MR = M > 16 ? 32 : 16;
-  auto lds_for = [&](int mr) { return dlm::lds_bytes((size_t)mr * H * es / 16, mr); };
-  if (lds_for(MR) > kLdsBudget) MR = 16;
-  if (lds_for(MR) > kLdsBudget)
-    return fail(DLM_ERR_SHAPE, "H=%lld too large: 16 hidden rows need %zu bytes of LDS (limit %zu)",
-                (long long)H, lds_for(MR), kLdsBudget);
-  const int n_rg = (int)((M + MR - 1) / MR);
-  int G_v = (kTargetWorkgroups / n_rg) / 8 * 8;
+  // each wavefront holds ceil(F / 8) hidden fragments per 16-row block in registers
+  const int64_t F = H * es / 64;                        // 64-byte fragments per row
+  const int64_t kfw = (F + dlm::kWaves - 1) / dlm::kWaves;
+  const int KFWM = kfw <= 2 ? 2 : kfw <= 8 ? 8 : kfw <= 16 ? 16 : 0;
+  if (!KFWM)
+    return fail(DLM_ERR_SHAPE, "H=%lld too large: at most %d for this dtype", (long long)H, 16 * 8 * 64 / es);
+  int NMB = M <= 16 ? 1 : M <= 32 ? 2 : 4;
+  if (NMB == 4 && KFWM == 16) NMB = 2;                  // register budget of the hidden fragments
+  const int MR = 16 * NMB;
+  const int64_t n_rg = (M + MR - 1) / MR;
+  int64_t G_v = (kTargetWorkgroups / n_rg) / 8 * 8;
   if (G_v < 8) G_v = 8;
-  const int64_t need = ((ntiles + dlm::kWaves - 1) / dlm::kWaves + 7) / 8 * 8;  // >= 1 tile per wave
-  if (G_v > need) G_v = (int)need;
+  const int64_t need = (ntiles + 7) / 8 * 8;            // no more ranges than tiles (rounded to 8)
+  if (G_v > need) G_v = need;
   if (G_v > dlm::kMaxVocabGroups) G_v = dlm::kMaxVocabGroups;
-  // each workgroup's W range must stay addressable by a 31-bit buffer offset
+  // buffer ranges are addressed with 31-bit offsets
   const int64_t range_bytes = ((ntiles + G_v - 1) / G_v) * dlm::kTileRows * H * es;
   if (range_bytes >= (1ll << 31) - 64)
     return fail(DLM_ERR_SHAPE, "V*H too large: %lld bytes of W per workgroup", (long long)range_bytes);
-  if ((int64_t)n_rg * G_v > (1ll << 30)) return fail(DLM_ERR_SHAPE, "too many rows");
-  p->MR = MR;
-  p->n_rg = n_rg;
-  p->G_v = G_v;
+  if ((n_rg * MR) * H * es >= (1ll << 31) || n_rg * MR * G_v * 16 >= (1ll << 31))
+    return fail(DLM_ERR_SHAPE, "B*L*H too large");
+  p->NMB = NMB;
+  p->KFWM = KFWM;
+  p->n_rg = (int)n_rg;
+  p->G_v = (int)G_v;
   p->ntiles = (int)ntiles;
-  p->lds = lds_for(MR);
-  p->ws = kTicketBytes + (size_t)n_rg * G_v * MR * 16;
+  p->lds = dlm::lds_bytes(NMB);
+  p->ws = kTicketBytes + (size_t)n_rg * MR * G_v * 16;
   return DLM_OK;
 }
 
@@ -122,29 +126,27 @@ int pack_rules(const dlm_policy* pol, bool need_credit_state, const void* credit
   return DLM_OK;
 }
 
-template <class T, int MR>
+template <class T, int NMB, int KFWM>
 int launch_step(const dlm::StepArgs& a, const Plan& p, hipStream_t stream) {
-  // Raise the kernel's dynamic-LDS limit once per device (idempotent; a race only repeats it).
-  static std::atomic<uint64_t> attr_set{0};
-  auto kern = dlm::step_kernel<T, MR>;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(DLM_ERR_HIP, "hipGetDevice failed");
-  }
-  const uint64_t bit = 1ull << (dev & 63);
-  if (!(attr_set.load(std::memory_order_relaxed) & bit)) {
-    if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kLdsBudget) != hipSuccess) {
-      (void)hipGetLastError();
-      return fail(DLM_ERR_HIP, "hipFuncSetAttribute(max dynamic LDS = %zu) failed", kLdsBudget);
-    }
-    attr_set.fetch_or(bit, std::memory_order_relaxed);
-  }
-  hipLaunchKernelGGL(kern, dim3(p.n_rg * p.G_v), dim3(dlm::kThreads), p.lds, stream, a);
+  hipLaunchKernelGGL((dlm::step_kernel<T, NMB, KFWM>), dim3(p.n_rg * p.G_v), dim3(dlm::kThreads), p.lds, stream, a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DLM_ERR_HIP, "step kernel launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+template <class T>
+int launch_step_for(const dlm::StepArgs& a, const Plan& p, hipStream_t stream) {
+  switch (p.NMB * 100 + p.KFWM) {
+    case 102: return launch_step<T, 1, 2>(a, p, stream);
+    case 108: return launch_step<T, 1, 8>(a, p, stream);
+    case 116: return launch_step<T, 1, 16>(a, p, stream);
+    case 202: return launch_step<T, 2, 2>(a, p, stream);
+    case 208: return launch_step<T, 2, 8>(a, p, stream);
+    case 216: return launch_step<T, 2, 16>(a, p, stream);
+    case 402: return launch_step<T, 4, 2>(a, p, stream);
+    case 408: return launch_step<T, 4, 8>(a, p, stream);
+    default: return fail(DLM_ERR_SHAPE, "no kernel for NMB=%d KFWM=%d", p.NMB, p.KFWM);
+  }
 }
 
 int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::CommitArgs c, bool commit) {
@@ -172,9 +174,7 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   c.flags = (commit ? dlm::kFlagCommit : 0u) | (commit ? (pol->flags & DLM_AUTO_ADVANCE) : 0u);
   a.c = c;
   hipStream_t stream = static_cast<hipStream_t>(pol->stream);
-  if (pol->dtype == DLM_BF16)
-    return p.MR == 32 ? launch_step<uint16_t, 32>(a, p, stream) : launch_step<uint16_t, 16>(a, p, stream);
-  return p.MR == 32 ? launch_step<float, 32>(a, p, stream) : launch_step<float, 16>(a, p, stream);
+  return pol->dtype == DLM_BF16 ? launch_step_for<uint16_t>(a, p, stream) : launch_step_for<float>(a, p, stream);
 }
 
 }  // namespace

@@ -20,13 +20,14 @@ constexpr int kThreads = kWaves * 64; // workgroup size
 constexpr int kTileRows = 16;         // vocabulary rows per MFMA tile
 constexpr int kPrefetch = 16;         // 16-byte W fragments in flight per lane
 constexpr int kRowsPerStage = 1024;   // finalize: rows staged in LDS at a time
-constexpr int kMergeLanes = 16;       // finalize: lanes merging one row
-constexpr int kMaxVocabGroups = kMergeLanes * 16;
+constexpr int kRowBatch = 4;          // finalize: rows per wavefront with loads in flight together
+constexpr int kMaxVocabGroups = 256;  // vocabulary ranges (records per row) at most
 constexpr unsigned kFlagCommit = 1u << 16;  // internal: run the commit policies
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
 struct Rule {
   int kind;
@@ -49,22 +50,20 @@ struct CommitArgs {
   uint8_t rule_of[DLM_MAX_SEQS];
 };
 
-// LDS: area A holds the hidden rows (phases 1-2) and later the finalize stage (conf + token of
-// kRowsPerStage rows); area B the per-wavefront statistics of phase 3.  Sizes in 16-byte units.
-__host__ __device__ constexpr size_t lds_area_a(size_t h_vec) {
-  return h_vec > (size_t)kRowsPerStage / 2 ? h_vec : (size_t)kRowsPerStage / 2;
-}
-__host__ __device__ constexpr size_t lds_bytes(size_t h_vec, int MR) {
-  return (lds_area_a(h_vec) + (size_t)kWaves * MR) * 16;
+// LDS of the step kernel for NMB 16-row blocks: two buffers of per-wavefront partial logits
+// (8 waves x NMB x 1 KB each), reused for the per-slot statistics and the finalize stage.
+__host__ __device__ constexpr size_t lds_bytes(int NMB) {
+  return (size_t)2 * kWaves * NMB * 1024 > (size_t)kRowsPerStage * 8 ? (size_t)2 * kWaves * NMB * 1024
+                                                                      : (size_t)kRowsPerStage * 8;
 }
 
 struct StepArgs {
   const void* hidden;  // [M][H]
   const void* W;       // [V][H]
-  float4* partials;    // [n_rg][G_v][MR] statistics of each vocabulary range
+  float4* partials;    // [n_rg * 16 * NMB][G_v] statistics record of each (row, vocabulary range)
   unsigned* ticket;    // completion counter, zero between calls
   int H, V, M;
-  int n_rg;            // row groups of MR rows
+  int n_rg;            // row groups of 16 * NMB rows
   int G_v;             // vocabulary ranges (multiple of 8)
   int ntiles;          // ceil(V / 16)
   CommitArgs c;
@@ -80,6 +79,63 @@ struct Stats {
 };
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- cross-lane exchange on a 64-lane wavefront -------------------------------------------------
+// Within a row of 16 lanes: DPP quad permutes and row mirrors.  Across rows: the gfx950 row-swap
+// permutes, which hand each lane its own value and its partner row's value; applying a symmetric
+// operation to the pair gives every lane the combined result.
+enum : int { kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140 };
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(float, dpp<CTRL>(__builtin_bit_cast(int, x)));
+}
+
+// (value of this lane's row pair partner) for rows 16 (W = 16) or 32 (W = 32) apart, as a pair
+// (lower row's value, upper row's value) identical in both rows
+template <int W>
+__device__ __forceinline__ void row_swap(int x, int& lo, int& hi) {
+  const auto r = W == 16 ? __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false)
+                         : __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+  lo = (int)r[0];
+  hi = (int)r[1];
+}
+
+template <class Op>
+__device__ __forceinline__ float wave_allreduce(float x, Op op) {
+  x = op(x, dpp<kDppXor1>(x));
+  x = op(x, dpp<kDppXor2>(x));
+  x = op(x, dpp<kDppHalfMirror>(x));
+  x = op(x, dpp<kDppMirror>(x));
+  int lo, hi;
+  row_swap<16>(__builtin_bit_cast(int, x), lo, hi);
+  x = op(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+  row_swap<32>(__builtin_bit_cast(int, x), lo, hi);
+  return op(__builtin_bit_cast(float, lo), __builtin_bit_cast(float, hi));
+}
+
+__device__ __forceinline__ int wave_allreduce_min(int x) {
+  x = min(x, dpp<kDppXor1>(x));
+  x = min(x, dpp<kDppXor2>(x));
+  x = min(x, dpp<kDppHalfMirror>(x));
+  x = min(x, dpp<kDppMirror>(x));
+  int lo, hi;
+  row_swap<16>(x, lo, hi);
+  x = min(lo, hi);
+  row_swap<32>(x, lo, hi);
+  return min(lo, hi);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_allreduce(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  return wave_allreduce(x, [](float a, float b) { return a + b; });
+}
 
 __device__ __forceinline__ Stats stats_empty() {
   Stats t;
@@ -101,13 +157,37 @@ __device__ __forceinline__ Stats stats_merge(const Stats& a, const Stats& b) {
   return r;
 }
 
-__device__ __forceinline__ Stats stats_shfl_xor(const Stats& a, int off) {
+template <int CTRL>
+__device__ __forceinline__ Stats stats_dpp(const Stats& a) {
   Stats r;
-  r.m1 = __shfl_xor(a.m1, off);
-  r.s = __shfl_xor(a.s, off);
-  r.m2 = __shfl_xor(a.m2, off);
-  r.id = __shfl_xor(a.id, off);
+  r.m1 = dpp<CTRL>(a.m1);
+  r.s = dpp<CTRL>(a.s);
+  r.m2 = dpp<CTRL>(a.m2);
+  r.id = dpp<CTRL>(a.id);
   return r;
+}
+
+// Every lane of a 16-lane row ends with the merge of the row's 16 statistics (fixed order).
+__device__ __forceinline__ Stats stats_row16_merge(Stats t) {
+  t = stats_merge(t, stats_dpp<kDppXor1>(t));
+  t = stats_merge(t, stats_dpp<kDppXor2>(t));
+  t = stats_merge(t, stats_dpp<kDppHalfMirror>(t));
+  t = stats_merge(t, stats_dpp<kDppMirror>(t));
+  return t;
+}
+
+// Statistics records are exchanged between workgroups with 16-byte buffer accesses carrying the
+// device-scope coherence bit (the cache policy the compiler gives device-scope atomics): stores
+// are written through to the device coherence point and loads read from it, so no cache
+// write-back or invalidation is needed around the completion counter.
+constexpr int kDeviceCoherent = 16;   // cache-policy operand: device scope
+
+__device__ __forceinline__ void record_store(__amdgpu_buffer_rsrc_t r, unsigned off, float4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kDeviceCoherent);
+}
+
+__device__ __forceinline__ float4 record_load(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceCoherent));
 }
 
 __device__ __forceinline__ float4 stats_pack(const Stats& a) {
@@ -123,25 +203,44 @@ __device__ __forceinline__ Stats stats_unpack(const float4& v) {
   return t;
 }
 
-// Fold four logits of ascending ids v0..v0+3 (ids >= V are padding) into the running stats.
-__device__ __forceinline__ void stats_fold4(Stats& st, f32x4 z, int v0, int V) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) z[r] = (v0 + r < V) ? z[r] : -INFINITY;
-  const float mnew = fmaxf(st.m1, fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3])));
-  if (mnew == -INFINITY) return;  // nothing valid seen yet
+// Fold one logit z of id v (ids arrive in ascending order per thread) into the running stats.
+__device__ __forceinline__ void stats_fold1(Stats& st, float z, int v) {
+  const float mnew = fmaxf(st.m1, z);
   const float nb = mnew * kLog2e;
-  float s = st.s * ex2(fmaf(st.m1, kLog2e, -nb));
+  st.s = st.s * ex2(fmaf(st.m1, kLog2e, -nb)) + ex2(fmaf(z, kLog2e, -nb));
+  st.m2 = fmaxf(st.m2, fminf(z, st.m1));
+  if (z > st.m1) st.id = v;
+  st.m1 = mnew;
+}
+
+// Merge the records of one row held by a wavefront (record g = lane + 64*i) into one result:
+// the maximum first, then the rescaled sum and the lowest id attaining the maximum, then the
+// second-largest logit (the winning record's own runner-up, or another record's maximum).
+// Every lane ends with the result; the summation order is fixed.
+__device__ __forceinline__ Stats merge_records(const float4 (&r)[kMaxVocabGroups / 64]) {
+  constexpr int N = kMaxVocabGroups / 64;
+  float m = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s += ex2(fmaf(z[r], kLog2e, -nb));
+  for (int i = 0; i < N; ++i) m = fmaxf(m, r[i].x);
+  const float M = wave_max(m);
+  float s = 0.f;
+  int id = 0x7fffffff;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    st.m2 = fmaxf(st.m2, fminf(z[r], st.m1));
-    if (z[r] > st.m1) {
-      st.m1 = z[r];
-      st.id = v0 + r;
-    }
+  for (int i = 0; i < N; ++i) {
+    if (r[i].y != 0.f) s += r[i].y * ex2((r[i].x - M) * kLog2e);
+    if (r[i].x == M) id = min(id, __float_as_int(r[i].z));
   }
-  st.s = s;
+  s = wave_sum(s);
+  id = wave_allreduce_min(id);
+  float sec = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < N; ++i) sec = fmaxf(sec, (r[i].x == M && __float_as_int(r[i].z) == id) ? r[i].w : r[i].x);
+  Stats t;
+  t.m1 = M;
+  t.s = s;
+  t.id = id;
+  t.m2 = wave_max(sec);
+  return t;
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -184,17 +283,8 @@ __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
 // Lane holding the largest value; the lowest lane wins a tie.
 __device__ __forceinline__ int argmax_lane(float v) {
-  int idx = __lane_id();
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const float ov = __shfl_xor(v, off);
-    const int oi = __shfl_xor(idx, off);
-    if (ov > v || (ov == v && oi < idx)) {
-      v = ov;
-      idx = oi;
-    }
-  }
-  return idx;
+  const float m = wave_max(v);
+  return wave_allreduce_min(v == m ? (int)__lane_id() : 64);
 }
 
 // Hierarchical decoding on the 64-bit mask U: the maximal masked runs are the top-level regions;
@@ -236,15 +326,43 @@ __device__ __forceinline__ uint64_t hierarchical_commit(uint64_t U, float conf, 
   return committed;
 }
 
+// State of one position of a sequence as the commit reads it (lane = position).
+struct SeqState {
+  bool masked;
+  int st[DLM_CREDIT_SLOTS];
+  float sc[DLM_CREDIT_SLOTS];
+};
+
+__device__ __forceinline__ SeqState load_seq_state(const CommitArgs& a, int b) {
+  const int l = __lane_id();
+  const size_t row = (size_t)b * a.L + l;
+  SeqState s;
+  s.masked = l < a.L && a.mask[row] != 0;
+#pragma unroll
+  for (int i = 0; i < DLM_CREDIT_SLOTS; ++i) {
+    s.st[i] = -1;
+    s.sc[i] = 0.f;
+  }
+  if (a.credit != nullptr && l < a.L) {
+#pragma unroll
+    for (int i = 0; i < DLM_CREDIT_SLOTS; ++i) {
+      const dlm_credit_slot cs = a.credit[row * DLM_CREDIT_SLOTS + i];
+      s.st[i] = cs.token;
+      s.sc[i] = cs.credit;
+    }
+  }
+  return s;
+}
+
 // One sequence on one wavefront: policy, outputs and state update.
-__device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok) {
+__device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok, const SeqState& in_state) {
   const int l = __lane_id();
   const bool in = l < a.L;
   const size_t row = (size_t)b * a.L + l;
   const Rule R = a.rules[a.rule_of[b]];
   if (!in) conf = -INFINITY;
 
-  bool masked = in && a.mask[row] != 0;
+  bool masked = in_state.masked;
   uint64_t U = ballot(masked);
   const bool advance = U == 0ull && (a.flags & DLM_AUTO_ADVANCE);
   if (advance) {
@@ -256,13 +374,10 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok)
   int st[DLM_CREDIT_SLOTS];
   float sc[DLM_CREDIT_SLOTS];
   const bool has_credit = a.credit != nullptr;
-  if (has_credit && in) {
 #pragma unroll
-    for (int i = 0; i < DLM_CREDIT_SLOTS; ++i) {
-      const dlm_credit_slot cs = a.credit[row * DLM_CREDIT_SLOTS + i];
-      st[i] = advance ? -1 : cs.token;
-      sc[i] = advance ? 0.f : cs.credit;
-    }
+  for (int i = 0; i < DLM_CREDIT_SLOTS; ++i) {
+    st[i] = advance ? -1 : in_state.st[i];
+    sc[i] = advance ? 0.f : in_state.sc[i];
   }
 
   uint64_t C = 0;
@@ -334,26 +449,33 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok)
 // ----------------------------------------------------------------------------------------------
 // The fused step kernel.
 //
-// Grid: G_v vocabulary ranges x n_rg row groups, one workgroup each, 8 wavefronts.  Workgroup
-// ids are dealt round-robin over the 8 XCDs; the row groups of one vocabulary range are placed
-// on the same XCD back to back so the repeated W reads of a range hit that XCD's L2.
+// Grid: G_v vocabulary ranges x n_rg row groups of MR = 16*NMB hidden rows, one workgroup of 8
+// wavefronts each.  Workgroup ids are dealt round-robin over the 8 XCDs; the row groups of one
+// vocabulary range sit on the same XCD back to back, so repeated W reads of a range hit its L2.
 //
-// Phase 1: the row group's hidden rows go to LDS in MFMA fragment order.
-// Phase 2: each wavefront streams the W tiles (16 vocab rows) of its share of the range straight
-//          from HBM into registers (kPrefetch fragments in flight), multiplies them with the
-//          hidden fragments on the matrix cores and folds every finished tile into per-lane
-//          online-softmax statistics.
-// Phase 3: lanes, then wavefronts merge their statistics; one record per row goes to memory.
-// Phase 4: the last workgroup to finish (completion counter) merges the records of every row in
-//          a fixed order, derives conf / token / gap and runs each sequence's commit policy.
+// Streaming: the 8 wavefronts share every 16-row vocabulary tile.  Wavefront w owns the K
+// fragments w, w+8, w+16, ... of each row (so together they sweep each row left to right) and
+// keeps the matching hidden-state fragments in registers for the whole kernel.  W fragments go
+// straight from HBM into a ring of registers (RING loads in flight per lane) and through the
+// matrix cores.  At the end of a tile each wavefront leaves its partial logits in LDS; after one
+// barrier every thread sums the 8 partials of its (row, vocabulary slot) and folds the logit into
+// its own online-softmax statistics (double-buffered LDS, one barrier per tile).
+//
+// Then the statistics of each row are merged inside the workgroup and one record per row goes to
+// the device coherence point; the last workgroup to finish (completion counter) merges the
+// records of every row in a fixed order, derives conf / token / gap and runs each sequence's
+// commit policy on one wavefront.
 // ----------------------------------------------------------------------------------------------
-template <class T, int MR>
+template <class T, int NMB, int KFWM>
 __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   extern __shared__ uint4 smem[];
   using E = Elem<T>;
-  constexpr int NMB = MR / 16;                  // 16-row blocks of hidden rows
-  constexpr int CH = 16 / E::kBytes;            // elements per 16-byte chunk
-  constexpr int KF = 4 * CH;                    // K covered by one fragment
+  constexpr int MR = 16 * NMB;                           // hidden rows of the row group
+  constexpr int RING = KFWM > (NMB * KFWM >= 32 ? 8 : kPrefetch) ? KFWM : (NMB * KFWM >= 32 ? 8 : kPrefetch);  // in flight per lane
+  constexpr int G = RING / KFWM;                         // tiles per unrolled ring pass
+  constexpr int LOGITS = kTileRows * MR;                 // logits of one tile
+  constexpr int P = (LOGITS + kThreads - 1) / kThreads;  // logit slots per thread
+  static_assert(RING % KFWM == 0, "ring must hold whole tiles");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the loop scalar
 
@@ -363,158 +485,180 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   const int gv = (slot / a.n_rg) * 8 + xcd;
 
   const int H = a.H;
-  const int F = H / KF;                          // fragments per row
-  const int hchunks = H / CH;                    // 16-byte chunks per hidden row
-  uint4* lds_h = smem;                           // [F][NMB][64] fragments
-  const size_t h_vec = (size_t)MR * hchunks;     // hidden-state area, in 16-byte units
-  float4* red = reinterpret_cast<float4*>(smem + lds_area_a(h_vec));  // [kWaves][MR] statistics
+  const int F = H / (4 * (16 / E::kBytes));              // 64-byte fragments per row
+  const unsigned row_bytes = (unsigned)H * E::kBytes;
+  const unsigned kOOB = 0x80000000u;                     // beyond any range: loads return 0
+  const unsigned lane_off = (lane & 15) * row_bytes + (lane >> 4) * 16u;
 
-  // ---- phase 1: hidden rows of this group -> LDS, straight from memory (no registers) -------
-  // One wavefront instruction fills one 1 KB fragment block (kf, mb): lane l brings row
-  // mb*16 + l%16, 16-byte chunk kf*4 + l/16.  Rows past M fall outside the buffer range and
-  // arrive as zeros.
-  {
-    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<void*>(a.hidden), 0, a.M * hchunks * 16, 0x00020000);
-    const int nblk = F * NMB;
-    for (int p = wave; p < nblk; p += kWaves) {
-      const int kf = p / NMB, mb = p - kf * NMB;
-      const unsigned r = (unsigned)(rg * MR + mb * 16 + (lane & 15));
-      const unsigned off = (r * (unsigned)hchunks + (unsigned)(kf * 4 + (lane >> 4))) * 16u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          hrs, (__attribute__((address_space(3))) void*)(lds_h + (size_t)p * 64), 16, off, 0, 0, 0);
-    }
-  }
-
-  // ---- phase 2 set-up; the first W loads overlap the hidden-state fill -----------------------
-  const int t_begin = (int)((long long)gv * a.ntiles / a.G_v);
-  const int t_end = (int)((long long)(gv + 1) * a.ntiles / a.G_v);
+  // ---- this workgroup's tiles and its W range ----------------------------------------------
+  // range index q: each XCD owns a contiguous eighth of the ranges, so the short ranges of the
+  // even split spread evenly over the XCDs
+  const int q = (gv & 7) * (a.G_v >> 3) + (gv >> 3);
+  const int t_begin = (int)((long long)q * a.ntiles / a.G_v);
+  const int t_end = (int)((long long)(q + 1) * a.ntiles / a.G_v);
   const int nloc = t_end - t_begin;
-  const int ntw = nloc > wave ? (nloc - wave + kWaves - 1) / kWaves : 0;
-  const int Q = ntw * F;
-  const int Qp = (Q + kPrefetch - 1) / kPrefetch * kPrefetch;
+  const int nloc_p = (nloc + G - 1) / G * G;
   const long long row0 = (long long)t_begin * kTileRows;
   const long long row_end = min((long long)a.V, (long long)t_end * kTileRows);
-  const long long nbytes = row_end > row0 ? (row_end - row0) * H * E::kBytes : 0;
-  const char* wbase = static_cast<const char*>(a.W) + row0 * H * E::kBytes;
-  const __amdgpu_buffer_rsrc_t rsrc =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(wbase), 0, (int)nbytes, 0x00020000);
-  const unsigned row_bytes = (unsigned)H * E::kBytes;
-  const unsigned tile_stride = (unsigned)kWaves * kTileRows * row_bytes;
-  const unsigned frag_bytes = KF * E::kBytes;
-  const unsigned kOOB = 0x80000000u;             // beyond any range: loads return 0, no traffic
-  unsigned ld_off = (unsigned)(wave * kTileRows + (lane & 15)) * row_bytes + (lane >> 4) * 16u;
-  int ld_q = 0, ld_kf = 0;
-  auto next_off = [&]() -> unsigned {
-    const unsigned o = ld_q < Q ? ld_off + (unsigned)ld_kf * frag_bytes : kOOB;
-    ++ld_q;
-    if (++ld_kf == F) {
-      ld_kf = 0;
-      ld_off += tile_stride;
-    }
-    return o;
+  const long long nbytes = row_end > row0 ? (row_end - row0) * row_bytes : 0;
+  const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<char*>(static_cast<const char*>(a.W) + row0 * row_bytes), 0, (int)nbytes, 0x00020000);
+
+  // byte offset of fragment kf = j*8 + wave of tile t (zero-filled past the range or the row)
+  auto w_off = [&](int t, int j) -> unsigned {
+    const int kf = j * kWaves + wave;
+    return (t < nloc && kf < F) ? (unsigned)t * kTileRows * row_bytes + lane_off + (unsigned)kf * 64u : kOOB;
   };
-  uint4 ring[kPrefetch];
-#pragma unroll
-  for (int j = 0; j < kPrefetch; ++j) ring[j] = buffer_load16(rsrc, next_off());
 
-  __syncthreads();
-
-  // ---- phase 2: stream W ----------------------------------------------------------------------
-  Stats st[NMB];
+  // ---- hidden fragments of this wavefront's K positions, in registers ------------------------
+  // rows past M and fragments past F read as zero (outside the buffer range)
+  uint4 hreg[KFWM][NMB];
+  {
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(a.hidden), 0, a.M * (int)row_bytes, 0x00020000);
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) st[mb] = stats_empty();
+    for (int j = 0; j < KFWM; ++j) {
+      const int kf = j * kWaves + wave;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const unsigned row = (unsigned)(rg * MR + mb * 16 + (lane & 15));
+        const unsigned off = row * row_bytes + (unsigned)kf * 64u + (lane >> 4) * 16u;
+        hreg[j][mb] = buffer_load16(hrs, kf < F ? off : kOOB);
+      }
+    }
+  }
+  // The hidden loads go out before the ring, so waiting for the oldest ring slot implies them.
+  __builtin_amdgcn_sched_barrier(0);
+  // ring slot u*KFWM + j always holds fragment j of a tile congruent to u modulo G
+  uint4 ring[RING];
+#pragma unroll
+  for (int u = 0; u < G; ++u)
+#pragma unroll
+    for (int j = 0; j < KFWM; ++j) {
+      ring[u * KFWM + j] = buffer_load16(wrs, w_off(u, j));
+      __builtin_amdgcn_sched_barrier(0);  // slot order = issue order
+    }
+
+  // ---- stream the tiles -------------------------------------------------------------------------
+  float* red = reinterpret_cast<float*>(smem);           // [2][kWaves][NMB][64 lanes][4] partials
+  Stats st[P];
+#pragma unroll
+  for (int p = 0; p < P; ++p) st[p] = stats_empty();
   f32x4 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  int kf = 0, tile_j = 0;
-  for (int q0 = 0; q0 < Qp; q0 += kPrefetch) {
+
+  for (int r0 = 0; r0 < nloc_p; r0 += G) {
 #pragma unroll
-    for (int j = 0; j < kPrefetch; ++j) {
-      // consume slot j, then refill it: the slot keeps its registers across iterations
-      const uint4* hp = lds_h + (size_t)kf * NMB * 64 + lane;
+    for (int u = 0; u < G; ++u) {
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) acc[mb] = E::mma(ring[j], hp[mb * 64], acc[mb]);
-      ring[j] = buffer_load16(rsrc, next_off());
-      if (++kf == F) {
-        kf = 0;
-        if (tile_j < ntw) {
-          const int v0 = (t_begin + wave + kWaves * tile_j) * kTileRows + 4 * (lane >> 4);
+      for (int j = 0; j < KFWM; ++j) {
 #pragma unroll
-          for (int mb = 0; mb < NMB; ++mb) stats_fold4(st[mb], acc[mb], v0, a.V);
+        for (int mb = 0; mb < NMB; ++mb) acc[mb] = E::mma(ring[u * KFWM + j], hreg[j][mb], acc[mb]);
+        ring[u * KFWM + j] = buffer_load16(wrs, w_off(r0 + u + G, j));
+        __builtin_amdgcn_sched_barrier(0);  // keep consume-then-refill order: the wait stays RING-1 deep
+      }
+      // tile r done: partials to LDS, one barrier, every thread folds its logit slots
+      const int r = r0 + u;
+      float* buf = red + (r & 1) * (kWaves * NMB * 256);
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        *reinterpret_cast<f32x4*>(buf + ((wave * NMB + mb) * 64 + lane) * 4) = acc[mb];
+        acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      __syncthreads();
+      if (r < nloc) {
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const int f = tid + p * kThreads;          // slot: (mb, lane, component) of the tile
+          if (f < LOGITS) {
+            const int mb = f >> 8, rest = f & 255;
+            float z = 0.f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) z += buf[(w * NMB + mb) * 256 + rest];
+            const int v = (t_begin + r) * kTileRows + 4 * (rest >> 6) + (rest & 3);
+            if (v < a.V) stats_fold1(st[p], z, v);
+          }
         }
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        ++tile_j;
       }
     }
   }
 
-  // ---- phase 3: lanes -> wavefront -> workgroup ------------------------------------------------
+  // ---- merge each row's 16 slots inside the workgroup; one record per row -----------------------
+  __syncthreads();
+  float4* slots = reinterpret_cast<float4*>(smem);       // [LOGITS] statistics, by slot
 #pragma unroll
-  for (int mb = 0; mb < NMB; ++mb) {
-    st[mb] = stats_merge(st[mb], stats_shfl_xor(st[mb], 16));
-    st[mb] = stats_merge(st[mb], stats_shfl_xor(st[mb], 32));
-  }
-  if (lane < 16) {
-#pragma unroll
-    for (int mb = 0; mb < NMB; ++mb) red[wave * MR + mb * 16 + lane] = stats_pack(st[mb]);
+  for (int p = 0; p < P; ++p) {
+    const int f = tid + p * kThreads;
+    if (f < LOGITS) slots[f] = stats_pack(st[p]);
   }
   __syncthreads();
-  if (tid < MR) {
-    Stats t = stats_unpack(red[tid]);
-    for (int w = 1; w < kWaves; ++w) t = stats_merge(t, stats_unpack(red[w * MR + tid]));
-    a.partials[((size_t)rg * a.G_v + gv) * MR + tid] = stats_pack(t);
-    __threadfence();
+  const __amdgpu_buffer_rsrc_t rec = __builtin_amdgcn_make_buffer_rsrc(
+      a.partials, 0, a.n_rg * MR * a.G_v * 16, 0x00020000);
+  for (int rr = wave * 4 + (lane >> 4); rr < MR; rr += kWaves * 4) {   // 4 rows per wavefront pass
+    // slot of contributor k = lane%16 of row rr: vocabulary sub-row 4*(k/4) + k%4 of the tile
+    const int k = lane & 15;
+    const int f = (rr >> 4) * 256 + 64 * (k >> 2) + 4 * (rr & 15) + (k & 3);
+    const Stats t = stats_row16_merge(stats_unpack(slots[f]));
+    if (k == 0) record_store(rec, (unsigned)((((size_t)rg * MR + rr) * a.G_v + gv) * 16), stats_pack(t));
   }
+  // The records must be complete before this workgroup is counted; device-scope stores need no
+  // cache write-back, only the wait for their acknowledgement.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // ---- phase 4: the last workgroup merges every row and commits -------------------------------
+  // ---- the last workgroup merges every row and commits ------------------------------------------
   // Wrapping increment: the counter runs 0 .. gridDim.x-1 and the last arrival puts it back to 0,
   // so a workspace that starts zeroed is zero again between calls.
   __shared__ int s_last;
-  if (tid == 0) {
-    const unsigned prev = __builtin_amdgcn_atomic_inc32(a.ticket, gridDim.x - 1, __ATOMIC_ACQ_REL, "agent");
-    s_last = prev == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-
-  float* s_conf = reinterpret_cast<float*>(smem);            // reuses the hidden-state area
-  int* s_tok = reinterpret_cast<int*>(smem) + kRowsPerStage;
   const CommitArgs& c = a.c;
   const bool do_commit = (c.flags & kFlagCommit) != 0;
+  if (tid == 0) {
+    const unsigned prev = __builtin_amdgcn_atomic_inc32(a.ticket, gridDim.x - 1, __ATOMIC_RELAXED, "agent");
+    s_last = prev == gridDim.x - 1;
+  }
+  // While the counter answers, each wavefront fetches the state of the sequence it would commit
+  // first (only the last workgroup uses it; the others drop it).
+  SeqState pre;
+  if (do_commit && wave < c.B) pre = load_seq_state(c, wave);
+  __syncthreads();
+  if (!s_last) return;
+
+  float* s_conf = reinterpret_cast<float*>(smem);        // reuses the partials area
+  int* s_tok = reinterpret_cast<int*>(smem) + kRowsPerStage;
   const int seq_per_stage = max(1, kRowsPerStage / c.L);
-  const int sub = tid % kMergeLanes;
   for (int b0 = 0; b0 < c.B; b0 += seq_per_stage) {
     const int b1 = min(c.B, b0 + seq_per_stage);
     const int r_first = b0 * c.L, nrows = (b1 - b0) * c.L;
-    for (int rr0 = 0; rr0 < nrows; rr0 += kThreads / kMergeLanes) {  // same trip count for all
-      const int rr = rr0 + tid / kMergeLanes;
-      const bool valid = rr < nrows;
-      const int row = r_first + (valid ? rr : 0);
-      const int g_rg = row / MR, ri = row % MR;
-      const float4* src = a.partials + (size_t)g_rg * a.G_v * MR + ri;
-      float4 buf[kMaxVocabGroups / kMergeLanes];
+    // one wavefront per row, kRowBatch rows with all their record loads in flight together
+    for (int rr0 = wave * kRowBatch; rr0 < nrows; rr0 += kWaves * kRowBatch) {
+      float4 buf[kRowBatch][kMaxVocabGroups / 64];
 #pragma unroll
-      for (int i = 0; i < kMaxVocabGroups / kMergeLanes; ++i) {
-        const int g = sub + i * kMergeLanes;
-        buf[i] = g < a.G_v ? src[(size_t)g * MR] : stats_pack(stats_empty());
+      for (int j = 0; j < kRowBatch; ++j) {
+        const int rr = rr0 + j;
+        const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * a.G_v * 16);
+#pragma unroll
+        for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
+          const int g = lane + 64 * i;
+          buf[j][i] = g < a.G_v ? record_load(rec, src + 16u * g) : stats_pack(stats_empty());
+        }
       }
-      Stats t = stats_unpack(buf[0]);
 #pragma unroll
-      for (int i = 1; i < kMaxVocabGroups / kMergeLanes; ++i) t = stats_merge(t, stats_unpack(buf[i]));
+      for (int j = 0; j < kRowBatch; ++j) {
+        const int rr = rr0 + j;
+        float4 row_stats[kMaxVocabGroups / 64];
 #pragma unroll
-      for (int off = kMergeLanes / 2; off >= 1; off >>= 1) t = stats_merge(t, stats_shfl_xor(t, off));
-      if (valid && sub == 0) {
-        const float conf = 1.f / t.s;
-        const float gap = t.m1 - t.m2;
-        s_conf[rr] = conf;
-        s_tok[rr] = t.id;
-        if (c.out_conf) c.out_conf[row] = conf;
-        if (c.out_gap) c.out_gap[row] = gap;
-        if (!do_commit) c.out_tokens[row] = t.id;
+        for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
+        const Stats t = merge_records(row_stats);
+        if (rr < nrows && lane == 0) {
+          const int row = r_first + rr;
+          const float conf = 1.f / t.s;
+          s_conf[rr] = conf;
+          s_tok[rr] = t.id;
+          if (c.out_conf) c.out_conf[row] = conf;
+          if (c.out_gap) c.out_gap[row] = t.m1 - t.m2;
+          if (!do_commit) c.out_tokens[row] = t.id;
+        }
       }
     }
     __syncthreads();
@@ -522,7 +666,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
       for (int b = b0 + wave; b < b1; b += kWaves) {
         const int off = (b - b0) * c.L + lane;
         const bool in = lane < c.L;
-        commit_sequence(c, b, in ? s_conf[off] : 0.f, in ? s_tok[off] : 0);
+        const SeqState sq = b == wave ? pre : load_seq_state(c, b);
+        commit_sequence(c, b, in ? s_conf[off] : 0.f, in ? s_tok[off] : 0, sq);
       }
     }
     __syncthreads();
@@ -536,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs a, co
   const int l = threadIdx.x & 63;
   const bool in = l < a.L;
   const size_t row = (size_t)b * a.L + l;
-  commit_sequence(a, b, in ? conf[row] : 0.f, in ? tok[row] : 0);
+  commit_sequence(a, b, in ? conf[row] : 0.f, in ? tok[row] : 0, load_seq_state(a, b));
 }
 
 // dlm_workspace_init: zero fill.

@@ -52,13 +52,14 @@ def test_header_constants_match_binding():
 
 
 def test_workspace_sizes():
-    # ticket line (256 B) + one 16-byte record per (row group, vocabulary range, row slot)
-    assert nat.dlm_workspace_bytes(1, 32, 2048, 126464, nat.DLM_BF16) == 256 + 1 * 256 * 32 * 16
-    assert nat.dlm_workspace_bytes(1, 64, 2048, 126464, nat.DLM_BF16) == 256 + 2 * 128 * 32 * 16
-    assert nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_F32) == 256 + 1 * 8 * 16 * 16
-    assert nat.dlm_workspace_bytes(16, 32, 2048, 157184, nat.DLM_BF16) > 0
+    # counter line (256 B) + one 16-byte record per (padded row, vocabulary range); rows are
+    # padded to 16, 32 or 64 per row group and there are at most 256 vocabulary ranges
+    assert nat.dlm_workspace_bytes(1, 32, 2048, 126464, nat.DLM_BF16) == 256 + 32 * 256 * 16
+    assert nat.dlm_workspace_bytes(1, 64, 2048, 126464, nat.DLM_BF16) == 256 + 64 * 256 * 16
+    assert nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_F32) == 256 + 16 * 64 * 16      # 64 tiles
+    assert nat.dlm_workspace_bytes(16, 32, 2048, 157184, nat.DLM_BF16) == 256 + 512 * 32 * 16
     for bad in [(0, 8, 64, 64, 0), (1, 65, 64, 64, 0), (1, 8, 48, 64, 0), (1, 8, 64, 0, 0), (1, 8, 64, 64, 5),
-                (257, 8, 64, 64, 1), (1, 8, 1 << 20, 64, 1)]:
+                (257, 8, 64, 64, 1), (1, 8, 1 << 20, 64, 1), (1, 8, 4128, 64, 1), (1, 8, 2080, 64, 0)]:
         assert nat.dlm_workspace_bytes(*bad) == 0, bad
 
 
