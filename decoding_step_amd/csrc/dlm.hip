@@ -36,6 +36,7 @@ constexpr int kTargetWorkgroups = 256;   // one per compute unit on MI355X
 
 // Launch geometry of one step, a pure function of the shapes (so the workspace size is too).
 struct Plan {
+  bool gemm = false; // many rows: GEMM-shaped head + separate finalize kernel
   int NMB = 0;       // 16-row blocks of hidden rows per workgroup (1, 2 or 4)
   int KFWM = 0;      // K fragments per wavefront per tile, rounded up (2, 8 or 16)
   int n_rg = 0;      // row groups
@@ -57,6 +58,23 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
   const int64_t M = B * L;
   const int64_t ntiles = (V + dlm::kTileRows - 1) / dlm::kTileRows;
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
+  if (dtype == DLM_BF16 && M > 64 && H % 128 == 0 && V * H * 2 < (1ll << 31) - 64 && M * H * 2 < (1ll << 31)) {
+    // GEMM-shaped path: 128-row vocabulary tiles against 512-row groups
+    const int64_t nt = (V + dlm::kGemmBN - 1) / dlm::kGemmBN;
+    const int64_t n_rg = (M + dlm::kGemmRows - 1) / dlm::kGemmRows;
+    int64_t G_t = kTargetWorkgroups / n_rg;
+    if (G_t < 1) G_t = 1;
+    if (G_t > nt) G_t = nt;
+    if (G_t > dlm::kMaxVocabGroups) G_t = dlm::kMaxVocabGroups;
+    if (n_rg * dlm::kGemmRows * G_t * 16 >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large");
+    p->gemm = true;
+    p->n_rg = (int)n_rg;
+    p->G_v = (int)G_t;
+    p->ntiles = (int)nt;
+    p->lds = 0;
+    p->ws = kTicketBytes + (size_t)n_rg * dlm::kGemmRows * G_t * 16;
+    return DLM_OK;
+  }
   // each wavefront holds ceil(F / 8) hidden fragments per 16-row block in registers
   const int64_t F = H * es / 64;                        // 64-byte fragments per row
   const int64_t kfw = (F + dlm::kWaves - 1) / dlm::kWaves;
@@ -174,6 +192,26 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   c.flags = (commit ? dlm::kFlagCommit : 0u) | (commit ? (pol->flags & DLM_AUTO_ADVANCE) : 0u);
   a.c = c;
   hipStream_t stream = static_cast<hipStream_t>(pol->stream);
+  if (p.gemm) {
+    dlm::GemmArgs g;
+    g.hidden = hidden;
+    g.W = W;
+    g.records = a.partials;
+    g.H = a.H;
+    g.V = a.V;
+    g.M = a.M;
+    g.n_rg = p.n_rg;
+    g.G_t = p.G_v;
+    g.ntiles = p.ntiles;
+    hipLaunchKernelGGL(dlm::gemm_stats_kernel, dim3(p.n_rg * p.G_v), dim3(dlm::kGemmThreads), 0, stream, g);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(DLM_ERR_HIP, "gemm kernel launch: %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(dlm::finalize_kernel, dim3(c.B), dim3(dlm::kThreads), 0, stream, a.c, a.partials, p.G_v,
+                       p.n_rg * dlm::kGemmRows);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(DLM_ERR_HIP, "finalize kernel launch: %s", hipGetErrorString(e));
+    return ok();
+  }
   return pol->dtype == DLM_BF16 ? launch_step_for<uint16_t>(a, p, stream) : launch_step_for<float>(a, p, stream);
 }
 

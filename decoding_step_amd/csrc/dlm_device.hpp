@@ -447,6 +447,67 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 }
 
 // ----------------------------------------------------------------------------------------------
+// Final merge + commit of sequences [b_begin, b_end): row r's G records sit at r*G .. r*G+G-1 of
+// `rec`.  One wavefront per row (kRowBatch rows with all their loads in flight together) merges
+// the records in a fixed order; conf / token go to LDS, then one wavefront per sequence commits.
+// `pre` is the state this wavefront already fetched for sequence `pre_b` (or pre_b = -1).
+// Called by a whole workgroup; `smem` needs kRowsPerStage * 8 bytes.
+// ----------------------------------------------------------------------------------------------
+__device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t rec, int G, int b_begin, int b_end,
+                                   uint4* smem, const SeqState& pre, int pre_b) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool do_commit = (c.flags & kFlagCommit) != 0;
+  float* s_conf = reinterpret_cast<float*>(smem);
+  int* s_tok = reinterpret_cast<int*>(smem) + kRowsPerStage;
+  const int seq_per_stage = max(1, kRowsPerStage / c.L);
+  for (int b0 = b_begin; b0 < b_end; b0 += seq_per_stage) {
+    const int b1 = min(b_end, b0 + seq_per_stage);
+    const int r_first = b0 * c.L, nrows = (b1 - b0) * c.L;
+    for (int rr0 = wave * kRowBatch; rr0 < nrows; rr0 += kWaves * kRowBatch) {
+      float4 buf[kRowBatch][kMaxVocabGroups / 64];
+#pragma unroll
+      for (int j = 0; j < kRowBatch; ++j) {
+        const int rr = rr0 + j;
+        const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * G * 16);
+#pragma unroll
+        for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
+          const int g = lane + 64 * i;
+          buf[j][i] = g < G ? record_load(rec, src + 16u * g) : stats_pack(stats_empty());
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kRowBatch; ++j) {
+        const int rr = rr0 + j;
+        float4 row_stats[kMaxVocabGroups / 64];
+#pragma unroll
+        for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
+        const Stats t = merge_records(row_stats);
+        if (rr < nrows && lane == 0) {
+          const int row = r_first + rr;
+          const float conf = 1.f / t.s;
+          s_conf[rr] = conf;
+          s_tok[rr] = t.id;
+          if (c.out_conf) c.out_conf[row] = conf;
+          if (c.out_gap) c.out_gap[row] = t.m1 - t.m2;
+          if (!do_commit) c.out_tokens[row] = t.id;
+        }
+      }
+    }
+    __syncthreads();
+    if (do_commit) {
+      for (int b = b0 + wave; b < b1; b += kWaves) {
+        const int off = (b - b0) * c.L + lane;
+        const bool in = lane < c.L;
+        const SeqState sq = b == pre_b ? pre : load_seq_state(c, b);
+        commit_sequence(c, b, in ? s_conf[off] : 0.f, in ? s_tok[off] : 0, sq);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ----------------------------------------------------------------------------------------------
 // The fused step kernel.
 //
 // Grid: G_v vocabulary ranges x n_rg row groups of MR = 16*NMB hidden rows, one workgroup of 8
@@ -624,54 +685,208 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  float* s_conf = reinterpret_cast<float*>(smem);        // reuses the partials area
-  int* s_tok = reinterpret_cast<int*>(smem) + kRowsPerStage;
-  const int seq_per_stage = max(1, kRowsPerStage / c.L);
-  for (int b0 = 0; b0 < c.B; b0 += seq_per_stage) {
-    const int b1 = min(c.B, b0 + seq_per_stage);
-    const int r_first = b0 * c.L, nrows = (b1 - b0) * c.L;
-    // one wavefront per row, kRowBatch rows with all their record loads in flight together
-    for (int rr0 = wave * kRowBatch; rr0 < nrows; rr0 += kWaves * kRowBatch) {
-      float4 buf[kRowBatch][kMaxVocabGroups / 64];
+  finalize_sequences(c, rec, a.G_v, 0, c.B, smem, pre, wave < c.B ? wave : -1);
+}
+
+// ----------------------------------------------------------------------------------------------
+// GEMM-shaped LM head for many rows (B*L > 64, bf16): the work crosses the MFMA ridge, so W must
+// be reused across all rows instead of being re-streamed per row group.
+//
+// A work unit is a 128-row vocabulary tile against all rows of a 512-row group.  Four wavefronts
+// (one per SIMD, so each may hold 256 accumulator registers) own 128 hidden rows each and share
+// every W tile through LDS.  Per 64-element K stage:
+//   * W goes HBM -> registers (issued two stages ahead, non-temporal so it does not push the
+//     hidden rows out of L2) -> LDS in MFMA fragment order (double-buffered, one barrier per
+//     stage); a wavefront instruction writes one contiguous 1 KB fragment block;
+//   * hidden fragments stream from L2 through a register ring, one K16 step per slot;
+//   * 4 x 4 v_mfma_f32_32x32x16_bf16 per K16 step: acc[vb][hb] = W[32 vocab] x h[32 rows]^T.
+// Lane l of acc[vb][hb] register r holds vocabulary row 32vb + 8(r/4) + 4(l/32) + r%4 of the tile
+// against hidden row 32hb + l%32 of the wavefront: 64 logits of one row per lane and tile, in
+// ascending vocabulary order, folded into that row's running statistics at the end of the tile.
+// Each workgroup ends with one record per row; finalize_kernel merges them and commits.
+// ----------------------------------------------------------------------------------------------
+constexpr int kGemmWaves = 4;
+constexpr int kGemmThreads = kGemmWaves * 64;
+constexpr int kGemmBN = 128;                              // vocabulary rows per tile
+constexpr int kGemmHB = 4;                                // 32-row hidden blocks per wavefront
+constexpr int kGemmRowsPerWave = 32 * kGemmHB;
+constexpr int kGemmRows = kGemmWaves * kGemmRowsPerWave;  // hidden rows per row group (512)
+constexpr int kGemmBK = 64;                               // K per stage
+constexpr int kGemmWLoads = 16 / kGemmWaves;              // W fragment blocks per wavefront per stage
+constexpr int kNonTemporal = 2;                           // cache-policy operand: streaming
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct GemmArgs {
+  const void* hidden;  // [M][H] bf16
+  const void* W;       // [V][H] bf16
+  float4* records;     // [n_rg * 512][G_t]
+  int H, V, M;
+  int n_rg;            // row groups of 512 rows
+  int G_t;             // workgroups per row group
+  int ntiles;          // ceil(V / 128)
+};
+
+__device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+// Fold the 64 logits of hidden block HB held by this lane (ascending ids) into st, 16 at a time:
+// chunk maximum, one rescale of the running sum, then one exponential per logit.
+template <int HB>
+__device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kGemmHB], int v0, int V) {
 #pragma unroll
-      for (int j = 0; j < kRowBatch; ++j) {
-        const int rr = rr0 + j;
-        const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * a.G_v * 16);
+  for (int vb = 0; vb < 4; ++vb) {
+    float z[16];
+    float cm = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
-          const int g = lane + 64 * i;
-          buf[j][i] = g < a.G_v ? record_load(rec, src + 16u * g) : stats_pack(stats_empty());
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kRowBatch; ++j) {
-        const int rr = rr0 + j;
-        float4 row_stats[kMaxVocabGroups / 64];
-#pragma unroll
-        for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
-        const Stats t = merge_records(row_stats);
-        if (rr < nrows && lane == 0) {
-          const int row = r_first + rr;
-          const float conf = 1.f / t.s;
-          s_conf[rr] = conf;
-          s_tok[rr] = t.id;
-          if (c.out_conf) c.out_conf[row] = conf;
-          if (c.out_gap) c.out_gap[row] = t.m1 - t.m2;
-          if (!do_commit) c.out_tokens[row] = t.id;
-        }
-      }
+    for (int r = 0; r < 16; ++r) {
+      const int v = v0 + 32 * vb + 8 * (r >> 2) + (r & 3);
+      z[r] = v < V ? acc[vb][HB][r] : -INFINITY;
+      cm = fmaxf(cm, z[r]);
     }
-    __syncthreads();
-    if (do_commit) {
-      for (int b = b0 + wave; b < b1; b += kWaves) {
-        const int off = (b - b0) * c.L + lane;
-        const bool in = lane < c.L;
-        const SeqState sq = b == wave ? pre : load_seq_state(c, b);
-        commit_sequence(c, b, in ? s_conf[off] : 0.f, in ? s_tok[off] : 0, sq);
-      }
+    const float mnew = fmaxf(st.m1, cm);
+    if (mnew == -INFINITY) continue;                      // nothing valid yet
+    const float nb = mnew * kLog2e;
+    float sum = st.s * ex2(fmaf(st.m1, kLog2e, -nb));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      sum += ex2(fmaf(z[r], kLog2e, -nb));
+      st.m2 = fmaxf(st.m2, fminf(z[r], st.m1));
+      if (z[r] > st.m1) st.id = v0 + 32 * vb + 8 * (r >> 2) + (r & 3);
+      st.m1 = fmaxf(st.m1, z[r]);
     }
-    __syncthreads();
+    st.s = sum;
   }
+}
+
+template <int HB>
+__device__ __forceinline__ void fold_all(Stats (&st)[kGemmHB], const f32x16 (&acc)[4][kGemmHB], int v0, int V) {
+  fold_tile64<HB>(st[HB], acc, v0, V);
+  if constexpr (HB + 1 < kGemmHB) fold_all<HB + 1>(st, acc, v0, V);
+}
+
+__global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs a) {
+  __shared__ uint4 wbuf[2][16][64];                       // 2 stages x 16 fragment blocks x 1 KB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rg = blockIdx.x % a.n_rg, gi = blockIdx.x / a.n_rg;
+  const int nt = a.ntiles > gi ? (a.ntiles - gi + a.G_t - 1) / a.G_t : 0;   // tiles gi, gi+G_t, ...
+  const int S = a.H / kGemmBK;                            // stages per tile (even)
+  const int total = nt * S;
+  const unsigned row_bytes = (unsigned)a.H * 2u;
+  const unsigned kOOB = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t wrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), 0, (int)((unsigned)a.V * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t hrs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.hidden), 0, (int)((unsigned)a.M * row_bytes), 0x00020000);
+
+  // W fragment block p = kGemmWLoads*wave + i of stage s: K16 step ks = p/4, vocabulary block
+  // vb = p%4; lane l brings row 32vb + l%32 of the tile, 8 elements at K 64kk + 16ks + 8(l/32)
+  const int p0 = kGemmWLoads * wave;                      // first fragment block of this wavefront
+  auto w_off = [&](int s, int i) -> unsigned {
+    const int t = gi + (s / S) * a.G_t, kk = s % S;
+    const int p = p0 + i, ks = p >> 2, vb = p & 3;
+    const unsigned row = (unsigned)(t * kGemmBN + 32 * vb + (lane & 31));
+    const unsigned off = row * row_bytes + (unsigned)(kk * kGemmBK + 16 * ks + 8 * (lane >> 5)) * 2u;
+    return s < total ? off : kOOB;
+  };
+  // hidden fragment (K16 step kg, block hb): row 128w + 32hb + l%32, 8 elements at 16kg + 8(l/32)
+  const unsigned h_row0 = (unsigned)(rg * kGemmRows + wave * kGemmRowsPerWave + (lane & 31));
+  auto h_off = [&](int s, int ks, int hb) -> unsigned {
+    const int kg = (s % S) * 4 + ks;
+    const unsigned off = (h_row0 + 32u * hb) * row_bytes + (unsigned)(16 * kg + 8 * (lane >> 5)) * 2u;
+    return s < total ? off : kOOB;
+  };
+  auto w_load = [&](int s, int i) -> uint4 {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, w_off(s, i), 0, kNonTemporal));
+  };
+
+  uint4 wr[2][kGemmWLoads], hr[4][kGemmHB];
+  f32x16 acc[4][kGemmHB];
+  Stats st[kGemmHB];
+#pragma unroll
+  for (int hb = 0; hb < kGemmHB; ++hb) st[hb] = stats_empty();
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+    for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = f32x16{};
+
+  // prologue: W of stages 0 and 1, hidden of stage 0, stage 0 to LDS
+#pragma unroll
+  for (int i = 0; i < kGemmWLoads; ++i) wr[0][i] = w_load(0, i);
+#pragma unroll
+  for (int i = 0; i < kGemmWLoads; ++i) wr[1][i] = w_load(1, i);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int hb = 0; hb < kGemmHB; ++hb) hr[ks][hb] = buffer_load16(hrs, h_off(0, ks, hb));
+#pragma unroll
+  for (int i = 0; i < kGemmWLoads; ++i) wbuf[0][kGemmWLoads * wave + i][lane] = wr[0][i];
+
+  for (int ti = 0; ti < nt; ++ti) {
+    for (int kk0 = 0; kk0 < S; kk0 += 2) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {                       // stage s uses LDS buffer u and W slot u
+        const int s = ti * S + kk0 + u;
+        __syncthreads();                                  // stage s is in wbuf[u]; wbuf[u^1] is free
+#pragma unroll
+        for (int i = 0; i < kGemmWLoads; ++i) wr[u][i] = w_load(s + 2, i);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          uint4 af[4];
+#pragma unroll
+          for (int vb = 0; vb < 4; ++vb) af[vb] = wbuf[u][ks * 4 + vb][lane];
+#pragma unroll
+          for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+            for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = mma32(af[vb], hr[ks][hb], acc[vb][hb]);
+#pragma unroll
+          for (int hb = 0; hb < kGemmHB; ++hb) hr[ks][hb] = buffer_load16(hrs, h_off(s + 1, ks, hb));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < kGemmWLoads; ++i) wbuf[u ^ 1][kGemmWLoads * wave + i][lane] = wr[u ^ 1][i];  // stage s+1
+      }
+    }
+    // tile done: fold its logits, then restart the sums (the next tile's loads are in flight)
+    fold_all<0>(st, acc, (gi + ti * a.G_t) * kGemmBN + 4 * (lane >> 5), a.V);
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+      for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = f32x16{};
+  }
+
+  // lanes l and l+32 hold the same rows over different vocabulary ids: merge the pair, then
+  // lanes 0..31 write one record per row
+#pragma unroll
+  for (int hb = 0; hb < kGemmHB; ++hb) {
+    Stats lo, hi;
+    int x0, x1;
+    row_swap<32>(__float_as_int(st[hb].m1), x0, x1); lo.m1 = __int_as_float(x0); hi.m1 = __int_as_float(x1);
+    row_swap<32>(__float_as_int(st[hb].s), x0, x1);  lo.s = __int_as_float(x0);  hi.s = __int_as_float(x1);
+    row_swap<32>(__float_as_int(st[hb].m2), x0, x1); lo.m2 = __int_as_float(x0); hi.m2 = __int_as_float(x1);
+    row_swap<32>(st[hb].id, x0, x1);                 lo.id = x0;                 hi.id = x1;
+    const Stats t = stats_merge(lo, hi);
+    const unsigned row = h_row0 + 32u * hb;
+    if (lane < 32 && (int)row < a.M) a.records[(size_t)row * a.G_t + gi] = stats_pack(t);
+  }
+}
+
+// Merge + commit after gemm_stats_kernel: one workgroup per sequence.
+__global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, const float4* records, int G,
+                                                            int nrows_total) {
+  __shared__ uint4 stage[kRowsPerStage / 2];
+  const int b = blockIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rec =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
+  SeqState pre;
+  const bool do_commit = (c.flags & kFlagCommit) != 0;
+  if (do_commit && wave == 0) pre = load_seq_state(c, b);
+  finalize_sequences(c, rec, G, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // dlm_commit: conf / tokens given, one wavefront per sequence.
