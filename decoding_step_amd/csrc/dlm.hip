@@ -58,7 +58,7 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
   const int64_t M = B * L;
   const int64_t ntiles = (V + dlm::kTileRows - 1) / dlm::kTileRows;
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
-  if (dtype == DLM_BF16 && M > 64 && H % 128 == 0 && V * H * 2 < (1ll << 31) - 64 && M * H * 2 < (1ll << 31)) {
+  if (dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && M * H * 2 < (1ll << 31)) {
     // GEMM-shaped path: 128-row vocabulary tiles against 512-row groups
     const int64_t nt = (V + dlm::kGemmBN - 1) / dlm::kGemmBN;
     const int64_t n_rg = (M + dlm::kGemmRows - 1) / dlm::kGemmRows;

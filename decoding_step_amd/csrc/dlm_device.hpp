@@ -695,9 +695,8 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
 // A work unit is a 128-row vocabulary tile against all rows of a 512-row group.  Four wavefronts
 // (one per SIMD, so each may hold 256 accumulator registers) own 128 hidden rows each and share
 // every W tile through LDS.  Per 64-element K stage:
-//   * W goes HBM -> registers (issued two stages ahead, non-temporal so it does not push the
-//     hidden rows out of L2) -> LDS in MFMA fragment order (double-buffered, one barrier per
-//     stage); a wavefront instruction writes one contiguous 1 KB fragment block;
+//   * W goes HBM -> registers (issued four stages ahead) -> LDS in MFMA fragment order (four
+//     buffers, one barrier per stage); a wavefront instruction writes one 1 KB fragment block;
 //   * hidden fragments stream from L2 through a register ring, one K16 step per slot;
 //   * 4 x 4 v_mfma_f32_32x32x16_bf16 per K16 step: acc[vb][hb] = W[32 vocab] x h[32 rows]^T.
 // Lane l of acc[vb][hb] register r holds vocabulary row 32vb + 8(r/4) + 4(l/32) + r%4 of the tile
@@ -713,7 +712,6 @@ constexpr int kGemmRowsPerWave = 32 * kGemmHB;
 constexpr int kGemmRows = kGemmWaves * kGemmRowsPerWave;  // hidden rows per row group (512)
 constexpr int kGemmBK = 64;                               // K per stage
 constexpr int kGemmWLoads = 16 / kGemmWaves;              // W fragment blocks per wavefront per stage
-constexpr int kNonTemporal = 2;                           // cache-policy operand: streaming
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -732,32 +730,58 @@ __device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
                                                  0, 0, 0);
 }
 
-// Fold the 64 logits of hidden block HB held by this lane (ascending ids) into st, 16 at a time:
-// chunk maximum, one rescale of the running sum, then one exponential per logit.
+// Fold the 64 logits of hidden block HB held by this lane (ids ascending with (vb, r)) into st.
+// Four interleaved sub-chains (r % 4) keep the top-2 / arg-max tracking and the sums independent;
+// one maximum per 16 logits sets the exponent base.  Ids >= V (padding of the last tile) are skipped.
 template <int HB>
 __device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kGemmHB], int v0, int V) {
+  const bool full = v0 + kGemmBN - 4 <= V;                // every id of this lane is valid
 #pragma unroll
   for (int vb = 0; vb < 4; ++vb) {
     float z[16];
-    float cm = -INFINITY;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int v = v0 + 32 * vb + 8 * (r >> 2) + (r & 3);
-      z[r] = v < V ? acc[vb][HB][r] : -INFINITY;
-      cm = fmaxf(cm, z[r]);
+      z[r] = (full || v < V) ? acc[vb][HB][r] : -INFINITY;
     }
-    const float mnew = fmaxf(st.m1, cm);
+    float c1[4], c2[4];
+    int ci[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {                         // sub-chain j: r = j, j+4, j+8, j+12
+      c1[j] = -INFINITY;
+      c2[j] = -INFINITY;
+      ci[j] = 0x7fffffff;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = j + 4 * q;
+        c2[j] = fmaxf(c2[j], fminf(z[r], c1[j]));
+        if (z[r] > c1[j]) ci[j] = v0 + 32 * vb + 8 * q + j;
+        c1[j] = fmaxf(c1[j], z[r]);
+      }
+    }
+    // merge the sub-chains (ids interleave, so ties go to the lower id explicitly)
+    float m = c1[0], m2 = c2[0];
+    int id = ci[0];
+#pragma unroll
+    for (int j = 1; j < 4; ++j) {
+      m2 = fmaxf(fmaxf(m2, c2[j]), fminf(m, c1[j]));
+      id = c1[j] > m ? ci[j] : (c1[j] == m ? min(id, ci[j]) : id);
+      m = fmaxf(m, c1[j]);
+    }
+    const float mnew = fmaxf(st.m1, m);
     if (mnew == -INFINITY) continue;                      // nothing valid yet
     const float nb = mnew * kLog2e;
-    float sum = st.s * ex2(fmaf(st.m1, kLog2e, -nb));
+    float ps[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      sum += ex2(fmaf(z[r], kLog2e, -nb));
-      st.m2 = fmaxf(st.m2, fminf(z[r], st.m1));
-      if (z[r] > st.m1) st.id = v0 + 32 * vb + 8 * (r >> 2) + (r & 3);
-      st.m1 = fmaxf(st.m1, z[r]);
+    for (int j = 0; j < 4; ++j) {
+      ps[j] = 0.f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ps[j] += ex2(fmaf(z[j + 4 * q], kLog2e, -nb));
     }
-    st.s = sum;
+    st.s = st.s * ex2(fmaf(st.m1, kLog2e, -nb)) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
+    st.m2 = fmaxf(fmaxf(st.m2, m2), fminf(st.m1, m));
+    if (m > st.m1) st.id = id;                            // ids of this chunk exceed earlier ones
+    st.m1 = mnew;
   }
 }
 
@@ -768,7 +792,7 @@ __device__ __forceinline__ void fold_all(Stats (&st)[kGemmHB], const f32x16 (&ac
 }
 
 __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs a) {
-  __shared__ uint4 wbuf[2][16][64];                       // 2 stages x 16 fragment blocks x 1 KB
+  __shared__ uint4 wbuf[4][16][64];                       // 4 stages x 16 fragment blocks x 1 KB
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = blockIdx.x % a.n_rg, gi = blockIdx.x / a.n_rg;
@@ -800,10 +824,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
     return s < total ? off : kOOB;
   };
   auto w_load = [&](int s, int i) -> uint4 {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, w_off(s, i), 0, kNonTemporal));
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, w_off(s, i), 0, 0));
   };
 
-  uint4 wr[2][kGemmWLoads], hr[4][kGemmHB];
+  // W: 4-slot register ring (stage s+4 issued during stage s), 4 LDS buffers (stage s in buffer
+  // s%4, written at the end of stage s-2); hidden: one stage ahead; A fragments: one K16 step ahead.
+  // One barrier per stage, after its second K16 step, orders both the buffer that is read next
+  // (written at the end of stage s-1) and the one written next (last read in stage s-2).
+  uint4 wr[4][kGemmWLoads], hr[4][kGemmHB], af[2][4];
   f32x16 acc[4][kGemmHB];
   Stats st[kGemmHB];
 #pragma unroll
@@ -813,42 +841,52 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
 #pragma unroll
     for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = f32x16{};
 
-  // prologue: W of stages 0 and 1, hidden of stage 0, stage 0 to LDS
 #pragma unroll
-  for (int i = 0; i < kGemmWLoads; ++i) wr[0][i] = w_load(0, i);
+  for (int u = 0; u < 4; ++u)
 #pragma unroll
-  for (int i = 0; i < kGemmWLoads; ++i) wr[1][i] = w_load(1, i);
+    for (int i = 0; i < kGemmWLoads; ++i) wr[u][i] = w_load(u, i);
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
     for (int hb = 0; hb < kGemmHB; ++hb) hr[ks][hb] = buffer_load16(hrs, h_off(0, ks, hb));
 #pragma unroll
-  for (int i = 0; i < kGemmWLoads; ++i) wbuf[0][kGemmWLoads * wave + i][lane] = wr[0][i];
+  for (int u = 0; u < 2; ++u)
+#pragma unroll
+    for (int i = 0; i < kGemmWLoads; ++i) wbuf[u][kGemmWLoads * wave + i][lane] = wr[u][i];
+  __syncthreads();
+#pragma unroll
+  for (int vb = 0; vb < 4; ++vb) af[0][vb] = wbuf[0][vb][lane];
 
   for (int ti = 0; ti < nt; ++ti) {
-    for (int kk0 = 0; kk0 < S; kk0 += 2) {
+    for (int kk0 = 0; kk0 < S; kk0 += 4) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {                       // stage s uses LDS buffer u and W slot u
+      for (int u = 0; u < 4; ++u) {                       // stage s: LDS buffer u, W slot u
         const int s = ti * S + kk0 + u;
-        __syncthreads();                                  // stage s is in wbuf[u]; wbuf[u^1] is free
 #pragma unroll
-        for (int i = 0; i < kGemmWLoads; ++i) wr[u][i] = w_load(s + 2, i);
+        for (int i = 0; i < kGemmWLoads; ++i) wr[u][i] = w_load(s + 4, i);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-          uint4 af[4];
+          const int cur = ks & 1, nxt = cur ^ 1;
+          if (ks < 3) {
 #pragma unroll
-          for (int vb = 0; vb < 4; ++vb) af[vb] = wbuf[u][ks * 4 + vb][lane];
+            for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = wbuf[u][(ks + 1) * 4 + vb][lane];
+          }
 #pragma unroll
           for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
-            for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = mma32(af[vb], hr[ks][hb], acc[vb][hb]);
+            for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = mma32(af[cur][vb], hr[ks][hb], acc[vb][hb]);
 #pragma unroll
           for (int hb = 0; hb < kGemmHB; ++hb) hr[ks][hb] = buffer_load16(hrs, h_off(s + 1, ks, hb));
+          if (ks == 1) __syncthreads();
+          if (ks == 3) {                                  // next stage's first fragments
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = wbuf[(u + 1) & 3][vb][lane];
+          }
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int i = 0; i < kGemmWLoads; ++i) wbuf[u ^ 1][kGemmWLoads * wave + i][lane] = wr[u ^ 1][i];  // stage s+1
+        for (int i = 0; i < kGemmWLoads; ++i) wbuf[(u + 2) & 3][kGemmWLoads * wave + i][lane] = wr[(u + 2) & 3][i];
       }
     }
     // tile done: fold its logits, then restart the sums (the next tile's loads are in flight)
