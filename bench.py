@@ -19,6 +19,7 @@ bf16 MFMA) and ``cpu_baseline`` (the CPU oracle on a bounded sample).
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -44,6 +45,26 @@ def algorithmic_work(wl):
     bytes_ = wl.V * wl.H * es + M * wl.H * es + state
     flops = 2.0 * M * wl.V * wl.H
     return bytes_, flops
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("decoding_step_amd/csrc/dlm_device.hpp", "decoding_step_amd/csrc/dlm.hip"):
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, if it matches these kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"step_kernel_{workload}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
 
 
 def record_trajectory(wl, W, Wd, steps, dev):
@@ -174,7 +195,7 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": bytes_ / sec_per_step / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    roof["traffic"] = measured_traffic(wl.name)
     roof["kernel"] = "dlm::step_kernel (one launch per step)"
     roof["algorithmic_bytes_per_launch"] = bytes_
     roof["algorithmic_flops_per_launch"] = flops
