@@ -44,6 +44,7 @@ struct Plan {
   int ntiles = 0;    // 16-row vocabulary tiles
   size_t lds = 0;    // dynamic LDS bytes
   size_t ws = 0;     // workspace bytes
+  size_t packed_off = 0, packed_bytes = 0;  // GEMM path: fragment-ordered hidden rows in the workspace
 };
 
 int elem_bytes(int32_t dtype) { return dtype == DLM_BF16 ? 2 : dtype == DLM_F32 ? 4 : 0; }
@@ -58,7 +59,8 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
   const int64_t M = B * L;
   const int64_t ntiles = (V + dlm::kTileRows - 1) / dlm::kTileRows;
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
-  if (dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && M * H * 2 < (1ll << 31)) {
+  const int64_t m_pad = (M + 31) / 32 * 32;
+  if (dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && m_pad * H * 2 < (1ll << 31)) {
     // GEMM-shaped path: 128-row vocabulary tiles against 512-row groups
     const int64_t nt = (V + dlm::kGemmBN - 1) / dlm::kGemmBN;
     const int64_t n_rg = (M + dlm::kGemmRows - 1) / dlm::kGemmRows;
@@ -72,7 +74,10 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
     p->G_v = (int)G_t;
     p->ntiles = (int)nt;
     p->lds = 0;
-    p->ws = kTicketBytes + (size_t)n_rg * dlm::kGemmRows * G_t * 16;
+    // ticket | records [n_rg * 512][G_t] | hidden rows in fragment order, padded to 32 rows
+    p->packed_off = kTicketBytes + (size_t)n_rg * dlm::kGemmRows * G_t * 16;
+    p->packed_bytes = (size_t)m_pad * H * 2;
+    p->ws = p->packed_off + p->packed_bytes;
     return DLM_OK;
   }
   // each wavefront holds ceil(F / 8) hidden fragments per 16-row block in registers
@@ -193,8 +198,16 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   a.c = c;
   hipStream_t stream = static_cast<hipStream_t>(pol->stream);
   if (p.gemm) {
+    void* packed = static_cast<char*>(pol->workspace) + p.packed_off;
+    const int pack_blocks = (int)std::min<size_t>((p.packed_bytes / 16 + 255) / 256, 1024);
+    hipLaunchKernelGGL(dlm::pack_hidden_kernel, dim3(pack_blocks), dim3(256), 0, stream,
+                       static_cast<const uint4*>(hidden), static_cast<uint4*>(packed), a.M, a.H);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(DLM_ERR_HIP, "pack kernel launch: %s", hipGetErrorString(e));
     dlm::GemmArgs g;
-    g.hidden = hidden;
+    g.hidden_packed = packed;
+    g.packed_bytes = (unsigned)p.packed_bytes;
+    g.fold_gate = 0xffffffffu;
     g.W = W;
     g.records = a.partials;
     g.H = a.H;
@@ -204,7 +217,7 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     g.G_t = p.G_v;
     g.ntiles = p.ntiles;
     hipLaunchKernelGGL(dlm::gemm_stats_kernel, dim3(p.n_rg * p.G_v), dim3(dlm::kGemmThreads), 0, stream, g);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "gemm kernel launch: %s", hipGetErrorString(e));
     hipLaunchKernelGGL(dlm::finalize_kernel, dim3(c.B), dim3(dlm::kThreads), 0, stream, a.c, a.partials, p.G_v,
                        p.n_rg * dlm::kGemmRows);

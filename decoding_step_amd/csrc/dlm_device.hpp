@@ -11,6 +11,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "dlm.h"
 
 namespace dlm {
@@ -695,10 +697,22 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
 // A work unit is a 128-row vocabulary tile against all rows of a 512-row group.  Four wavefronts
 // (one per SIMD, so each may hold 256 accumulator registers) own 128 hidden rows each and share
 // every W tile through LDS.  Per 64-element K stage:
-//   * W goes HBM -> registers (issued four stages ahead) -> LDS in MFMA fragment order (four
-//     buffers, one barrier per stage); a wavefront instruction writes one 1 KB fragment block;
-//   * hidden fragments stream from L2 through a register ring, one K16 step per slot;
+//   * W moves HBM -> LDS by direct-to-LDS buffer loads, never through registers: each wavefront
+//     instruction brings 8 whole 128-byte row segments (fully used cache lines) into a ring of
+//     four 16 KB stage buffers, issued three stages before their use.  Inside a row the 16-byte
+//     chunks are permuted (chunk c of tile row r sits at slot c ^ swz(r)) so that the MFMA
+//     fragment reads hit 16 distinct bank groups per 16 lanes;
+//   * hidden rows are packed beforehand (pack_hidden_kernel) into MFMA fragment order, so each
+//     fragment is one contiguous 1 KB load from L2; they run kGemmHDepth stages ahead in registers;
 //   * 4 x 4 v_mfma_f32_32x32x16_bf16 per K16 step: acc[vb][hb] = W[32 vocab] x h[32 rows]^T.
+// Vector-memory loads retire in issue order, so a wait for a hidden fragment also waits for
+// every W load issued before it: the hidden fragments' lead bounds the W loads' latency cover.
+// (A two-stage lead measured slower than one: its 64 extra registers cost spills in the fold.)
+// One barrier per stage, after the second K16 step.  Before it each wavefront waits until its
+// own W loads for the next stage have landed (a counted wait: at least kGemmVmAfterW
+// vector-memory instructions are issued after them in program order); after it the wavefront
+// issues the W loads three stages ahead, into the buffer that every wavefront finished reading a
+// stage earlier.
 // Lane l of acc[vb][hb] register r holds vocabulary row 32vb + 8(r/4) + 4(l/32) + r%4 of the tile
 // against hidden row 32hb + l%32 of the wavefront: 64 logits of one row per lane and tile, in
 // ascending vocabulary order, folded into that row's running statistics at the end of the tile.
@@ -711,51 +725,89 @@ constexpr int kGemmHB = 4;                                // 32-row hidden block
 constexpr int kGemmRowsPerWave = 32 * kGemmHB;
 constexpr int kGemmRows = kGemmWaves * kGemmRowsPerWave;  // hidden rows per row group (512)
 constexpr int kGemmBK = 64;                               // K per stage
-constexpr int kGemmWLoads = 16 / kGemmWaves;              // W fragment blocks per wavefront per stage
+constexpr int kGemmRing = 4;                              // W stage buffers in LDS
+constexpr int kGemmWDma = kGemmBN / 8 / kGemmWaves;       // W load instructions per wavefront per stage
+constexpr int kGemmHDepth = 1;                            // stages of hidden fragments in flight
+// vector-memory instructions issued after a stage's W loads and before the wait that must cover
+// them: the rest of that stage (2 K16 steps x 4 hidden loads), one whole stage (16 hidden loads
+// + the next W loads) and the first half of the following one (8 hidden loads)
+constexpr int kGemmVmAfterW = 8 + (16 + kGemmWDma) + 8;
+static_assert(kGemmVmAfterW <= 63, "vmcnt holds at most 63");
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
-  const void* hidden;  // [M][H] bf16
-  const void* W;       // [V][H] bf16
-  float4* records;     // [n_rg * 512][G_t]
+  const void* hidden_packed;  // fragment-ordered hidden rows (pack_hidden_kernel), zero-padded to 32 rows
+  const void* W;              // [V][H] bf16
+  float4* records;            // [n_rg * 512][G_t]
   int H, V, M;
-  int n_rg;            // row groups of 512 rows
-  int G_t;             // workgroups per row group
-  int ntiles;          // ceil(V / 128)
+  int n_rg;                   // row groups of 512 rows
+  int G_t;                    // workgroups per row group
+  int ntiles;                 // ceil(V / 128)
+  unsigned packed_bytes;      // bytes of hidden_packed
+  unsigned fold_gate;         // all ones (see fold_tile64)
 };
+
+// Hidden rows -> MFMA fragment order: fragment (rb, kg) is 1 KB at (rb * H/16 + kg) * 1 KB, lane l
+// holding row 32rb + l%32, elements 16kg + 8(l/32) .. +8.  Rows past M are zero.
+__global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4* hp, int M, int H) {
+  const int KG = H / 16;
+  const size_t n = (size_t)((M + 31) / 32) * KG * 64;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+    const int l = (int)(i & 63);
+    const size_t f = i >> 6;
+    const int kg = (int)(f % KG), rb = (int)(f / KG);
+    const int row = 32 * rb + (l & 31);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < M) v = h[(size_t)row * (H / 8) + 2 * kg + (l >> 5)];
+    hp[i] = v;
+  }
+}
 
 __device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                  0, 0, 0);
 }
 
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding: vmcnt in bits 3:0 and
+// 15:14, export count 6:4 and LDS/scalar count 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // Fold the 64 logits of hidden block HB held by this lane (ids ascending with (vb, r)) into st.
 // Four interleaved sub-chains (r % 4) keep the top-2 / arg-max tracking and the sums independent;
-// one maximum per 16 logits sets the exponent base.  Ids >= V (padding of the last tile) are skipped.
+// one maximum per 16 logits sets the exponent base.  With the chain maximum c1 >= second c2, the
+// new second maximum after seeing z is the median of (c1, c2, z).  Logits at offsets >= lim from
+// v0 (ids >= V, last tile only) become -inf first.
+// Each 16-logit chunk sits behind its own bit of `gate` (all ones at run time): separate basic
+// blocks keep the compiler from interleaving chunks, which would hold 256 logits in registers.
 template <int HB>
-__device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kGemmHB], int v0, int V) {
-  const bool full = v0 + kGemmBN - 4 <= V;                // every id of this lane is valid
+__device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kGemmHB], int v0, int lim,
+                                            unsigned gate) {
 #pragma unroll
   for (int vb = 0; vb < 4; ++vb) {
+    if (!((gate >> (4 * HB + vb)) & 1u)) continue;
     float z[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int v = v0 + 32 * vb + 8 * (r >> 2) + (r & 3);
-      z[r] = (full || v < V) ? acc[vb][HB][r] : -INFINITY;
-    }
+    for (int r = 0; r < 16; ++r) z[r] = acc[vb][HB][r];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) z[r] = 32 * vb + 8 * (r >> 2) + (r & 3) < lim ? z[r] : -INFINITY;
     float c1[4], c2[4];
     int ci[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {                         // sub-chain j: r = j, j+4, j+8, j+12
-      c1[j] = -INFINITY;
+      c1[j] = z[j];
       c2[j] = -INFINITY;
-      ci[j] = 0x7fffffff;
+      ci[j] = v0 + 32 * vb + j;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int q = 1; q < 4; ++q) {
         const int r = j + 4 * q;
-        c2[j] = fmaxf(c2[j], fminf(z[r], c1[j]));
-        if (z[r] > c1[j]) ci[j] = v0 + 32 * vb + 8 * q + j;
+        c2[j] = __builtin_amdgcn_fmed3f(c1[j], c2[j], z[r]);
+        ci[j] = z[r] > c1[j] ? v0 + 32 * vb + 8 * q + j : ci[j];
         c1[j] = fmaxf(c1[j], z[r]);
       }
     }
@@ -769,69 +821,92 @@ __device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kG
       m = fmaxf(m, c1[j]);
     }
     const float mnew = fmaxf(st.m1, m);
-    if (mnew == -INFINITY) continue;                      // nothing valid yet
-    const float nb = mnew * kLog2e;
+    const float nb = mnew == -INFINITY ? 0.f : mnew * kLog2e;   // nothing valid yet: every term is 0
     float ps[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      ps[j] = 0.f;
+      ps[j] = ex2(fmaf(z[j], kLog2e, -nb));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) ps[j] += ex2(fmaf(z[j + 4 * q], kLog2e, -nb));
+      for (int q = 1; q < 4; ++q) ps[j] += ex2(fmaf(z[j + 4 * q], kLog2e, -nb));
     }
     st.s = st.s * ex2(fmaf(st.m1, kLog2e, -nb)) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     st.m2 = fmaxf(fmaxf(st.m2, m2), fminf(st.m1, m));
-    if (m > st.m1) st.id = id;                            // ids of this chunk exceed earlier ones
+    st.id = m > st.m1 ? id : st.id;                       // ids of this chunk exceed earlier ones
     st.m1 = mnew;
   }
 }
 
 template <int HB>
-__device__ __forceinline__ void fold_all(Stats (&st)[kGemmHB], const f32x16 (&acc)[4][kGemmHB], int v0, int V) {
-  fold_tile64<HB>(st[HB], acc, v0, V);
-  if constexpr (HB + 1 < kGemmHB) fold_all<HB + 1>(st, acc, v0, V);
+__device__ __forceinline__ void fold_all(Stats (&st)[kGemmHB], const f32x16 (&acc)[4][kGemmHB], int v0, int lim,
+                                         unsigned gate) {
+  fold_tile64<HB>(st[HB], acc, v0, lim, gate);
+  if constexpr (HB + 1 < kGemmHB) fold_all<HB + 1>(st, acc, v0, lim, gate);
 }
 
 __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs a) {
-  __shared__ uint4 wbuf[4][16][64];                       // 4 stages x 16 fragment blocks x 1 KB
+  // W stage buffers [row * 8 + permuted chunk], one array each so that the compiler can tell a
+  // buffer being filled from the one being read (it would otherwise wait for every fill)
+  __shared__ uint4 wring0[kGemmBN * 8], wring1[kGemmBN * 8], wring2[kGemmBN * 8], wring3[kGemmBN * 8];
+  auto ring = [&](int slot) -> uint4* { return slot == 0 ? wring0 : slot == 1 ? wring1 : slot == 2 ? wring2 : wring3; };
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rg = blockIdx.x % a.n_rg, gi = blockIdx.x / a.n_rg;
   const int nt = a.ntiles > gi ? (a.ntiles - gi + a.G_t - 1) / a.G_t : 0;   // tiles gi, gi+G_t, ...
-  const int S = a.H / kGemmBK;                            // stages per tile (even)
+  const int S = a.H / kGemmBK;                            // stages per tile (multiple of 4)
+  const int KG = a.H / 16;
   const int total = nt * S;
   const unsigned row_bytes = (unsigned)a.H * 2u;
-  const unsigned kOOB = 0x80000000u;
+  const unsigned kOOB = 0x80000000u;                      // beyond any range: loads return 0
   const __amdgpu_buffer_rsrc_t wrs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.W), 0, (int)((unsigned)a.V * row_bytes), 0x00020000);
   const __amdgpu_buffer_rsrc_t hrs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.hidden), 0, (int)((unsigned)a.M * row_bytes), 0x00020000);
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.hidden_packed), 0, (int)a.packed_bytes, 0x00020000);
 
-  // W fragment block p = kGemmWLoads*wave + i of stage s: K16 step ks = p/4, vocabulary block
-  // vb = p%4; lane l brings row 32vb + l%32 of the tile, 8 elements at K 64kk + 16ks + 8(l/32)
-  const int p0 = kGemmWLoads * wave;                      // first fragment block of this wavefront
-  auto w_off = [&](int s, int i) -> unsigned {
-    const int t = gi + (s / S) * a.G_t, kk = s % S;
-    const int p = p0 + i, ks = p >> 2, vb = p & 3;
-    const unsigned row = (unsigned)(t * kGemmBN + 32 * vb + (lane & 31));
-    const unsigned off = row * row_bytes + (unsigned)(kk * kGemmBK + 16 * ks + 8 * (lane >> 5)) * 2u;
-    return s < total ? off : kOOB;
+  // Addresses split into a per-lane constant (voffset) and a per-stage, wavefront-uniform part
+  // (soffset, kOOB past the last stage so the loads return zeros without touching memory).
+  // W load instruction i of this wavefront: tile rows 32w + 8i + l/8, lane l bringing chunk
+  // (l%8) ^ swz(row) of the stage's 128-byte segment, landing at LDS slot row * 8 + l%8, with
+  // swz(r) = (r ^ (r >> 3)) & 7.
+  unsigned w_voff[kGemmWDma];
+#pragma unroll
+  for (int i = 0; i < kGemmWDma; ++i) {
+    const int r = 32 * wave + 8 * i + (lane >> 3);
+    w_voff[i] = (unsigned)r * row_bytes + 16u * (unsigned)((lane & 7) ^ ((r ^ (r >> 3)) & 7));
+  }
+  // stage (tile index ti, K block kk) of this workgroup
+  auto w_soff = [&](int ti, int kk) -> unsigned {
+    const int s = ti * S + kk;
+    return s < total ? (unsigned)((gi + ti * a.G_t) * kGemmBN) * row_bytes + (unsigned)(kk * kGemmBK * 2) : kOOB;
   };
-  // hidden fragment (K16 step kg, block hb): row 128w + 32hb + l%32, 8 elements at 16kg + 8(l/32)
-  const unsigned h_row0 = (unsigned)(rg * kGemmRows + wave * kGemmRowsPerWave + (lane & 31));
-  auto h_off = [&](int s, int ks, int hb) -> unsigned {
-    const int kg = (s % S) * 4 + ks;
-    const unsigned off = (h_row0 + 32u * hb) * row_bytes + (unsigned)(16 * kg + 8 * (lane >> 5)) * 2u;
-    return s < total ? off : kOOB;
+  auto w_issue = [&](int slot, unsigned soff) {
+#pragma unroll
+    for (int i = 0; i < kGemmWDma; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          wrs, (__attribute__((address_space(3))) void*)(ring(slot) + (32 * wave + 8 * i) * 8), 16, w_voff[i], soff, 0,
+          0);
   };
-  auto w_load = [&](int s, int i) -> uint4 {
-    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(wrs, w_off(s, i), 0, 0));
+  // fragment reads: lane l, block vb, K16 step ks reads tile row r = 32vb + l%32, chunk
+  // c = 2ks + l/32, at slot r*8 + (c ^ swz(r)) = 256vb + 8(l%32) + (x_l ^ 2(ks ^ 2(vb&1))) with
+  // x_l = (l/32) ^ (l%8) ^ ((l/8)%4)
+  const int x_l = (lane >> 5) ^ (lane & 7) ^ ((lane >> 3) & 3);
+  int rd_base[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) rd_base[k] = 8 * (lane & 31) + (x_l ^ (2 * k));
+  auto w_frag = [&](int slot, int vb, int ks) -> uint4 {
+    return ring(slot)[rd_base[ks ^ (2 * (vb & 1))] + 256 * vb];
+  };
+  // hidden fragment (block hb, K16 step 4kk + ks) of this wavefront
+  const unsigned h_voff = ((unsigned)(16 * rg + 4 * wave) * (unsigned)KG) * 1024u + 16u * lane;
+  const unsigned hb_stride = (unsigned)KG * 1024u;        // bytes between 32-row blocks
+  auto h_soff = [&](int ti, int kk) -> unsigned {
+    return ti * S + kk < total ? (unsigned)(kk * 4) * 1024u : kOOB;
+  };
+  auto h_load = [&](unsigned soff, int ks, int hb) -> uint4 {
+    return __builtin_bit_cast(
+        uint4, __builtin_amdgcn_raw_buffer_load_b128(hrs, h_voff + (unsigned)(ks * 1024), soff + hb * hb_stride, 0));
   };
 
-  // W: 4-slot register ring (stage s+4 issued during stage s), 4 LDS buffers (stage s in buffer
-  // s%4, written at the end of stage s-2); hidden: one stage ahead; A fragments: one K16 step ahead.
-  // One barrier per stage, after its second K16 step, orders both the buffer that is read next
-  // (written at the end of stage s-1) and the one written next (last read in stage s-2).
-  uint4 wr[4][kGemmWLoads], hr[4][kGemmHB], af[2][4];
+  uint4 hr[kGemmHDepth][4][kGemmHB], af[2][4];
   f32x16 acc[4][kGemmHB];
   Stats st[kGemmHB];
 #pragma unroll
@@ -841,64 +916,87 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
 #pragma unroll
     for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = f32x16{};
 
+  // prologue: W stages 0..2, hidden stages 0 and 1, then the barrier that opens stage 0.  Every
+  // W load of the prologue has at least kGemmVmAfterW vector-memory instructions behind it by the
+  // barrier that needs it, as in the steady state.  (S >= 4, so stages 0..2 are in tile 0.)
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
+  for (int p = 0; p < 3; ++p) w_issue(p, w_soff(0, p));
 #pragma unroll
-    for (int i = 0; i < kGemmWLoads; ++i) wr[u][i] = w_load(u, i);
+  for (int p = 0; p < kGemmHDepth; ++p) {
+    const unsigned so = h_soff(0, p);
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks)
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-    for (int hb = 0; hb < kGemmHB; ++hb) hr[ks][hb] = buffer_load16(hrs, h_off(0, ks, hb));
+      for (int hb = 0; hb < kGemmHB; ++hb) hr[p][ks][hb] = h_load(so, ks, hb);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vmcnt<kGemmVmAfterW>();                            // W stage 0 landed
+  __builtin_amdgcn_s_waitcnt(0xc07f);                     // and no LDS access pending
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int u = 0; u < 2; ++u)
-#pragma unroll
-    for (int i = 0; i < kGemmWLoads; ++i) wbuf[u][kGemmWLoads * wave + i][lane] = wr[u][i];
-  __syncthreads();
-#pragma unroll
-  for (int vb = 0; vb < 4; ++vb) af[0][vb] = wbuf[0][vb][lane];
+  for (int vb = 0; vb < 4; ++vb) af[0][vb] = w_frag(0, vb, 0);
 
-  for (int ti = 0; ti < nt; ++ti) {
-    for (int kk0 = 0; kk0 < S; kk0 += 4) {
+  // four stages kk0 .. kk0+3 of tile ti; FIRST: the tile's first group, whose first K16 step
+  // starts the accumulators from zero
+  auto group = [&](int ti, int kk0, auto first) {
+    constexpr bool FIRST = decltype(first)::value;
+    const bool last4 = kk0 + 4 == S;                      // stages kk0+u+2 / +3 may wrap to tile ti+1
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {                       // stage s: LDS buffer u, W slot u
-        const int s = ti * S + kk0 + u;
+    for (int u = 0; u < 4; ++u) {                         // stage kk0+u: buffer u, hidden set u % depth
+      const int hp = u % kGemmHDepth;
+      const bool hw = last4 && u + kGemmHDepth >= 4, ww = last4 && u + 3 >= 4;
+      const unsigned hso = h_soff(ti + hw, kk0 + u + kGemmHDepth - (hw ? S : 0));
+      const unsigned wso = w_soff(ti + ww, kk0 + u + 3 - (ww ? S : 0));
 #pragma unroll
-        for (int i = 0; i < kGemmWLoads; ++i) wr[u][i] = w_load(s + 4, i);
-        __builtin_amdgcn_sched_barrier(0);
+      for (int ks = 0; ks < 4; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        if (ks < 3) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const int cur = ks & 1, nxt = cur ^ 1;
-          if (ks < 3) {
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = wbuf[u][(ks + 1) * 4 + vb][lane];
-          }
-#pragma unroll
-          for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-            for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = mma32(af[cur][vb], hr[ks][hb], acc[vb][hb]);
-#pragma unroll
-          for (int hb = 0; hb < kGemmHB; ++hb) hr[ks][hb] = buffer_load16(hrs, h_off(s + 1, ks, hb));
-          if (ks == 1) __syncthreads();
-          if (ks == 3) {                                  // next stage's first fragments
-#pragma unroll
-            for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = wbuf[(u + 1) & 3][vb][lane];
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = w_frag(u, vb, ks + 1);
         }
 #pragma unroll
-        for (int i = 0; i < kGemmWLoads; ++i) wbuf[(u + 2) & 3][kGemmWLoads * wave + i][lane] = wr[(u + 2) & 3][i];
+        for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+          for (int hb = 0; hb < kGemmHB; ++hb)
+            acc[vb][hb] = mma32(af[cur][vb], hr[hp][ks][hb], (FIRST && u == 0 && ks == 0) ? f32x16{} : acc[vb][hb]);
+#pragma unroll
+        for (int hb = 0; hb < kGemmHB; ++hb) hr[hp][ks][hb] = h_load(hso, ks, hb);   // kGemmHDepth stages ahead
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 1) {
+          // open the next stage: its W landed for every wavefront; buffer (u+3)&3 was last read
+          // in the previous stage, so the W loads three stages ahead may overwrite it
+          wait_vmcnt<kGemmVmAfterW>();
+          __builtin_amdgcn_s_waitcnt(0xc07f);
+          __builtin_amdgcn_s_barrier();
+          __builtin_amdgcn_sched_barrier(0);
+          w_issue((u + 3) & 3, wso);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if (ks == 3) {                                    // next stage's first fragments
+#pragma unroll
+          for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = w_frag((u + 1) & 3, vb, 0);
+        }
       }
     }
-    // tile done: fold its logits, then restart the sums (the next tile's loads are in flight)
-    fold_all<0>(st, acc, (gi + ti * a.G_t) * kGemmBN + 4 * (lane >> 5), a.V);
+  };
+
+  for (int ti = 0; ti < nt; ++ti) {
+    for (int kk0 = 0; kk0 < S; kk0 += 4) group(ti, kk0, std::false_type{});
+    // tile done: fold its logits (the next tile's loads are in flight)
+    const int t0 = (gi + ti * a.G_t) * kGemmBN;
+    const int v0 = t0 + 4 * (lane >> 5);
+    fold_all<0>(st, acc, v0, a.V - v0, a.fold_gate);  // ids >= V (last tile) are skipped
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
       for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = f32x16{};
   }
+  __builtin_amdgcn_s_waitcnt(0);                          // no load into LDS may outlive the workgroup
 
   // lanes l and l+32 hold the same rows over different vocabulary ids: merge the pair, then
   // lanes 0..31 write one record per row
+  const unsigned h_row0 = (unsigned)(rg * kGemmRows + wave * kGemmRowsPerWave + (lane & 31));
 #pragma unroll
   for (int hb = 0; hb < kGemmHB; ++hb) {
     Stats lo, hi;
