@@ -836,10 +836,14 @@ __device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kG
   }
 }
 
+// The running statistics live in LDS between folds (st[hb * 64 + lane]): they are touched once
+// per tile, and registers are what the streaming loop needs.
 template <int HB>
-__device__ __forceinline__ void fold_all(Stats (&st)[kGemmHB], const f32x16 (&acc)[4][kGemmHB], int v0, int lim,
+__device__ __forceinline__ void fold_all(float4* st, const f32x16 (&acc)[4][kGemmHB], int v0, int lim,
                                          unsigned gate) {
-  fold_tile64<HB>(st[HB], acc, v0, lim, gate);
+  Stats t = stats_unpack(st[HB * 64]);
+  fold_tile64<HB>(t, acc, v0, lim, gate);
+  st[HB * 64] = stats_pack(t);
   if constexpr (HB + 1 < kGemmHB) fold_all<HB + 1>(st, acc, v0, lim, gate);
 }
 
@@ -908,13 +912,10 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
 
   uint4 hr[kGemmHDepth][4][kGemmHB], af[2][4];
   f32x16 acc[4][kGemmHB];
-  Stats st[kGemmHB];
+  __shared__ float4 st_lds[kGemmWaves * kGemmHB * 64];  // running statistics, [wave][hb][lane]
+  float4* const st = st_lds + wave * (kGemmHB * 64) + lane;
 #pragma unroll
-  for (int hb = 0; hb < kGemmHB; ++hb) st[hb] = stats_empty();
-#pragma unroll
-  for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-    for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = f32x16{};
+  for (int hb = 0; hb < kGemmHB; ++hb) st[hb * 64] = stats_pack(stats_empty());
 
   // prologue: W stages 0..2, hidden stages 0 and 1, then the barrier that opens stage 0.  Every
   // W load of the prologue has at least kGemmVmAfterW vector-memory instructions behind it by the
@@ -982,15 +983,12 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
   };
 
   for (int ti = 0; ti < nt; ++ti) {
-    for (int kk0 = 0; kk0 < S; kk0 += 4) group(ti, kk0, std::false_type{});
+    group(ti, 0, std::true_type{});
+    for (int kk0 = 4; kk0 < S; kk0 += 4) group(ti, kk0, std::false_type{});
     // tile done: fold its logits (the next tile's loads are in flight)
     const int t0 = (gi + ti * a.G_t) * kGemmBN;
     const int v0 = t0 + 4 * (lane >> 5);
     fold_all<0>(st, acc, v0, a.V - v0, a.fold_gate);  // ids >= V (last tile) are skipped
-#pragma unroll
-    for (int vb = 0; vb < 4; ++vb)
-#pragma unroll
-      for (int hb = 0; hb < kGemmHB; ++hb) acc[vb][hb] = f32x16{};
   }
   __builtin_amdgcn_s_waitcnt(0);                          // no load into LDS may outlive the workgroup
 
@@ -1001,10 +999,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
   for (int hb = 0; hb < kGemmHB; ++hb) {
     Stats lo, hi;
     int x0, x1;
-    row_swap<32>(__float_as_int(st[hb].m1), x0, x1); lo.m1 = __int_as_float(x0); hi.m1 = __int_as_float(x1);
-    row_swap<32>(__float_as_int(st[hb].s), x0, x1);  lo.s = __int_as_float(x0);  hi.s = __int_as_float(x1);
-    row_swap<32>(__float_as_int(st[hb].m2), x0, x1); lo.m2 = __int_as_float(x0); hi.m2 = __int_as_float(x1);
-    row_swap<32>(st[hb].id, x0, x1);                 lo.id = x0;                 hi.id = x1;
+    const Stats sh = stats_unpack(st[hb * 64]);
+    row_swap<32>(__float_as_int(sh.m1), x0, x1); lo.m1 = __int_as_float(x0); hi.m1 = __int_as_float(x1);
+    row_swap<32>(__float_as_int(sh.s), x0, x1);  lo.s = __int_as_float(x0);  hi.s = __int_as_float(x1);
+    row_swap<32>(__float_as_int(sh.m2), x0, x1); lo.m2 = __int_as_float(x0); hi.m2 = __int_as_float(x1);
+    row_swap<32>(sh.id, x0, x1);                 lo.id = x0;                 hi.id = x1;
     const Stats t = stats_merge(lo, hi);
     const unsigned row = h_row0 + 32u * hb;
     if (lane < 32 && (int)row < a.M) a.records[(size_t)row * a.G_t + gi] = stats_pack(t);
