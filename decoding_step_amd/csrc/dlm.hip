@@ -36,7 +36,7 @@ constexpr int kTargetWorkgroups = 256;   // one per compute unit on MI355X
 
 // Launch geometry of one step, a pure function of the shapes (so the workspace size is too).
 struct Plan {
-  bool gemm = false; // many rows: GEMM-shaped head + separate finalize kernel
+  int gemm = 0;      // many rows: GEMM-shaped head + separate finalize kernel
   int NMB = 0;       // 16-row blocks of hidden rows per workgroup (1, 2 or 4)
   int KFWM = 0;      // K fragments per wavefront per tile, rounded up (2, 8 or 16)
   int n_rg = 0;      // row groups
@@ -61,21 +61,25 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
   const int64_t m_pad = (M + 31) / 32 * 32;
   if (dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && m_pad * H * 2 < (1ll << 31)) {
-    // GEMM-shaped path: 128-row vocabulary tiles against 512-row groups
-    const int64_t nt = (V + dlm::kGemmBN - 1) / dlm::kGemmBN;
-    const int64_t n_rg = (M + dlm::kGemmRows - 1) / dlm::kGemmRows;
+    // GEMM-shaped path: 256-row vocabulary tiles against 256-row groups; workgroups per row group
+    // a multiple of 8 where possible (so the groups of one tile can share an XCD)
+    const int64_t BN = dlm::GemmWide::BN;
+    const int64_t rows = dlm::GemmWide::Rows;
+    const int64_t nt = (V + BN - 1) / BN;
+    const int64_t n_rg = (M + rows - 1) / rows;
     int64_t G_t = kTargetWorkgroups / n_rg;
+    if (G_t >= 8) G_t = G_t / 8 * 8;
     if (G_t < 1) G_t = 1;
     if (G_t > nt) G_t = nt;
     if (G_t > dlm::kMaxVocabGroups) G_t = dlm::kMaxVocabGroups;
-    if (n_rg * dlm::kGemmRows * G_t * 16 >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large");
-    p->gemm = true;
+    if (n_rg * rows * G_t * 16 >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large");
+    p->gemm = 1;
     p->n_rg = (int)n_rg;
     p->G_v = (int)G_t;
     p->ntiles = (int)nt;
     p->lds = 0;
-    // ticket | records [n_rg * 512][G_t] | hidden rows in fragment order, padded to 32 rows
-    p->packed_off = kTicketBytes + (size_t)n_rg * dlm::kGemmRows * G_t * 16;
+    // ticket | records [n_rg * rows][G_t] | hidden rows in fragment order, padded to 32 rows
+    p->packed_off = kTicketBytes + (size_t)n_rg * rows * G_t * 16;
     p->packed_bytes = (size_t)m_pad * H * 2;
     p->ws = p->packed_off + p->packed_bytes;
     return DLM_OK;
@@ -216,11 +220,14 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     g.n_rg = p.n_rg;
     g.G_t = p.G_v;
     g.ntiles = p.ntiles;
-    hipLaunchKernelGGL(dlm::gemm_stats_kernel, dim3(p.n_rg * p.G_v), dim3(dlm::kGemmThreads), 0, stream, g);
+    const dim3 grid(p.n_rg * p.G_v), block(dlm::kGemmThreads);
+    const int rows = dlm::GemmWide::Rows;
+    const bool tail = a.V % dlm::GemmWide::BN != 0;
+    hipLaunchKernelGGL(tail ? dlm::gemm_wide_tail_kernel : dlm::gemm_wide_kernel, grid, block, 0, stream, g);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "gemm kernel launch: %s", hipGetErrorString(e));
     hipLaunchKernelGGL(dlm::finalize_kernel, dim3(c.B), dim3(dlm::kThreads), 0, stream, a.c, a.partials, p.G_v,
-                       p.n_rg * dlm::kGemmRows);
+                       p.n_rg * rows);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "finalize kernel launch: %s", hipGetErrorString(e));
     return ok();

@@ -694,58 +694,70 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
 // GEMM-shaped LM head for many rows (B*L > 64, bf16): the work crosses the MFMA ridge, so W must
 // be reused across all rows instead of being re-streamed per row group.
 //
-// A work unit is a 128-row vocabulary tile against all rows of a 512-row group.  Four wavefronts
-// (one per SIMD, so each may hold 256 accumulator registers) own 128 hidden rows each and share
-// every W tile through LDS.  Per 64-element K stage:
+// A work unit is a vocabulary tile against all rows of a row group.  Four wavefronts (one per SIMD,
+// so each may hold 256 accumulator registers) own the group's hidden rows in equal parts and share
+// every W tile through LDS (tile shapes: GemmShape).  Per 64-element K stage:
 //   * W moves HBM -> LDS by direct-to-LDS buffer loads, never through registers: each wavefront
 //     instruction brings 8 whole 128-byte row segments (fully used cache lines) into a ring of
-//     four 16 KB stage buffers, issued three stages before their use.  Inside a row the 16-byte
+//     four stage buffers, issued three stages before their use.  Inside a row the 16-byte
 //     chunks are permuted (chunk c of tile row r sits at slot c ^ swz(r)) so that the MFMA
 //     fragment reads hit 16 distinct bank groups per 16 lanes;
 //   * hidden rows are packed beforehand (pack_hidden_kernel) into MFMA fragment order, so each
-//     fragment is one contiguous 1 KB load from L2; they run kGemmHDepth stages ahead in registers;
-//   * 4 x 4 v_mfma_f32_32x32x16_bf16 per K16 step: acc[vb][hb] = W[32 vocab] x h[32 rows]^T.
+//     fragment is one contiguous 1 KB load from L2; they run G::HDepth stages ahead in registers;
+//   * VB x HB v_mfma_f32_32x32x16_bf16 per K16 step: acc[vb][hb] = W[32 vocab] x h[32 rows]^T.
 // Vector-memory loads retire in issue order, so a wait for a hidden fragment also waits for
 // every W load issued before it: the hidden fragments' lead bounds the W loads' latency cover.
-// (A two-stage lead measured slower than one: its 64 extra registers cost spills in the fold.)
 // One barrier per stage, after the second K16 step.  Before it each wavefront waits until its
-// own W loads for the next stage have landed (a counted wait: at least kGemmVmAfterW
+// own W loads for the next stage have landed (a counted wait: at least G::VmAfterW
 // vector-memory instructions are issued after them in program order); after it the wavefront
 // issues the W loads three stages ahead, into the buffer that every wavefront finished reading a
 // stage earlier.
+// With several row groups, the workgroups that share a vocabulary tile run on one XCD (block
+// indices 8 apart) at the same pace, so W is fetched from HBM once and re-read from that L2.
 // Lane l of acc[vb][hb] register r holds vocabulary row 32vb + 8(r/4) + 4(l/32) + r%4 of the tile
-// against hidden row 32hb + l%32 of the wavefront: 64 logits of one row per lane and tile, in
+// against hidden row 32hb + l%32 of the wavefront: 16 VB logits of one row per lane and tile, in
 // ascending vocabulary order, folded into that row's running statistics at the end of the tile.
 // Each workgroup ends with one record per row; finalize_kernel merges them and commits.
 // ----------------------------------------------------------------------------------------------
 constexpr int kGemmWaves = 4;
 constexpr int kGemmThreads = kGemmWaves * 64;
-constexpr int kGemmBN = 128;                              // vocabulary rows per tile
-constexpr int kGemmHB = 4;                                // 32-row hidden blocks per wavefront
-constexpr int kGemmRowsPerWave = 32 * kGemmHB;
-constexpr int kGemmRows = kGemmWaves * kGemmRowsPerWave;  // hidden rows per row group (512)
 constexpr int kGemmBK = 64;                               // K per stage
 constexpr int kGemmRing = 4;                              // W stage buffers in LDS
-constexpr int kGemmWDma = kGemmBN / 8 / kGemmWaves;       // W load instructions per wavefront per stage
-constexpr int kGemmHDepth = 1;                            // stages of hidden fragments in flight
-// vector-memory instructions issued after a stage's W loads and before the wait that must cover
-// them: the rest of that stage (2 K16 steps x 4 hidden loads), one whole stage (16 hidden loads
-// + the next W loads) and the first half of the following one (8 hidden loads)
-constexpr int kGemmVmAfterW = 8 + (16 + kGemmWDma) + 8;
-static_assert(kGemmVmAfterW <= 63, "vmcnt holds at most 63");
+
+// Tile shape: a wavefront owns VB 32-row vocabulary blocks x HB 32-row hidden blocks (VB * HB = 16
+// accumulator blocks = 256 AGPRs).  The shape in use is 8 x 2: few hidden rows per wavefront make
+// its hidden fragments a small register cost per stage of lead (measured against 4 x 4, which
+// reads each W fragment for 4 products instead of 2: as fast at 512 rows, slower at 256).
+template <int VB_, int HB_>
+struct GemmShape {
+  static constexpr int VB = VB_, HB = HB_;
+  static constexpr int BN = 32 * VB;                      // vocabulary rows per tile
+  static constexpr int RowsPerWave = 32 * HB;
+  static constexpr int Rows = kGemmWaves * RowsPerWave;   // hidden rows per row group
+  static constexpr int Slot = BN * 8;                     // 16-byte slots per W stage buffer
+  static constexpr int WDma = BN / 8 / kGemmWaves;        // W load instructions per wavefront per stage
+  static constexpr int HDepth = 4 / HB;                   // stages of hidden fragments in flight (64 VGPRs)
+  // vector-memory instructions issued after a stage's W loads and before the wait that must cover
+  // them: the rest of that stage (2 K16 steps of hidden loads), one whole stage (4 K16 steps of
+  // hidden loads + the next W loads) and the first half of the following one
+  static constexpr int VmAfterW = 2 * HB + (4 * HB + WDma) + 2 * HB;
+  static_assert(VB * HB == 16, "256 accumulator registers");
+  static_assert(VmAfterW <= 63, "vmcnt holds at most 63");
+};
+using GemmWide = GemmShape<8, 2>;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 struct GemmArgs {
   const void* hidden_packed;  // fragment-ordered hidden rows (pack_hidden_kernel), zero-padded to 32 rows
   const void* W;              // [V][H] bf16
-  float4* records;            // [n_rg * 512][G_t]
+  float4* records;            // [n_rg * rows per group][G_t]
   int H, V, M;
-  int n_rg;                   // row groups of 512 rows
+  int n_rg;                   // row groups
   int G_t;                    // workgroups per row group
-  int ntiles;                 // ceil(V / 128)
+  int ntiles;                 // ceil(V / tile rows)
   unsigned packed_bytes;      // bytes of hidden_packed
-  unsigned fold_gate;         // all ones (see fold_tile64)
+  unsigned fold_gate;         // all ones (see fold_tile)
 };
 
 // Hidden rows -> MFMA fragment order: fragment (rb, kg) is 1 KB at (rb * H/16 + kg) * 1 KB, lane l
@@ -778,36 +790,38 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Fold the 64 logits of hidden block HB held by this lane (ids ascending with (vb, r)) into st.
+// Fold the 16 VB logits of hidden block HB held by this lane (ids ascending with (vb, r)) into st.
 // Four interleaved sub-chains (r % 4) keep the top-2 / arg-max tracking and the sums independent;
 // one maximum per 16 logits sets the exponent base.  With the chain maximum c1 >= second c2, the
-// new second maximum after seeing z is the median of (c1, c2, z).  Logits at offsets >= lim from
-// v0 (ids >= V, last tile only) become -inf first.
+// new second maximum after seeing z is the median of (c1, c2, z).  With TAIL, logits at offsets
+// >= lim from v0 (ids >= V, last tile) become -inf first.
 // Each 16-logit chunk sits behind its own bit of `gate` (all ones at run time): separate basic
-// blocks keep the compiler from interleaving chunks, which would hold 256 logits in registers.
-template <int HB>
-__device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kGemmHB], int v0, int lim,
-                                            unsigned gate) {
+// blocks keep the compiler from interleaving chunks, which would hold every logit in registers.
+template <class G, int HB, bool TAIL>
+__device__ __forceinline__ void fold_tile(Stats& st, const f32x16 (&acc)[G::VB][G::HB], int v0, int lim,
+                                          unsigned gate) {
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) {
-    if (!((gate >> (4 * HB + vb)) & 1u)) continue;
+  for (int vb = 0; vb < G::VB; ++vb) {
+    if (!((gate >> (G::VB * HB + vb)) & 1u)) continue;
     float z[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) z[r] = acc[vb][HB][r];
+    if constexpr (TAIL) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) z[r] = 32 * vb + 8 * (r >> 2) + (r & 3) < lim ? z[r] : -INFINITY;
+      for (int r = 0; r < 16; ++r) z[r] = 32 * vb + 8 * (r >> 2) + (r & 3) < lim ? z[r] : -INFINITY;
+    }
     float c1[4], c2[4];
-    int ci[4];
+    int ci[4];                                            // offset of the chain maximum in the chunk
 #pragma unroll
     for (int j = 0; j < 4; ++j) {                         // sub-chain j: r = j, j+4, j+8, j+12
       c1[j] = z[j];
       c2[j] = -INFINITY;
-      ci[j] = v0 + 32 * vb + j;
+      ci[j] = j;
 #pragma unroll
       for (int q = 1; q < 4; ++q) {
         const int r = j + 4 * q;
         c2[j] = __builtin_amdgcn_fmed3f(c1[j], c2[j], z[r]);
-        ci[j] = z[r] > c1[j] ? v0 + 32 * vb + 8 * q + j : ci[j];
+        ci[j] = z[r] > c1[j] ? 8 * q + j : ci[j];
         c1[j] = fmaxf(c1[j], z[r]);
       }
     }
@@ -817,7 +831,8 @@ __device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kG
 #pragma unroll
     for (int j = 1; j < 4; ++j) {
       m2 = fmaxf(fmaxf(m2, c2[j]), fminf(m, c1[j]));
-      id = c1[j] > m ? ci[j] : (c1[j] == m ? min(id, ci[j]) : id);
+      const bool better = (c1[j] > m) | ((c1[j] == m) & (ci[j] < id));
+      id = better ? ci[j] : id;
       m = fmaxf(m, c1[j]);
     }
     const float mnew = fmaxf(st.m1, m);
@@ -831,34 +846,49 @@ __device__ __forceinline__ void fold_tile64(Stats& st, const f32x16 (&acc)[4][kG
     }
     st.s = st.s * ex2(fmaf(st.m1, kLog2e, -nb)) + ((ps[0] + ps[1]) + (ps[2] + ps[3]));
     st.m2 = fmaxf(fmaxf(st.m2, m2), fminf(st.m1, m));
-    st.id = m > st.m1 ? id : st.id;                       // ids of this chunk exceed earlier ones
+    st.id = m > st.m1 ? v0 + 32 * vb + id : st.id;        // ids of this chunk exceed earlier ones
     st.m1 = mnew;
   }
 }
 
 // The running statistics live in LDS between folds (st[hb * 64 + lane]): they are touched once
 // per tile, and registers are what the streaming loop needs.
-template <int HB>
-__device__ __forceinline__ void fold_all(float4* st, const f32x16 (&acc)[4][kGemmHB], int v0, int lim,
+template <class G, int HB, bool TAIL>
+__device__ __forceinline__ void fold_all(float4* st, const f32x16 (&acc)[G::VB][G::HB], int v0, int lim,
                                          unsigned gate) {
   Stats t = stats_unpack(st[HB * 64]);
-  fold_tile64<HB>(t, acc, v0, lim, gate);
+  fold_tile<G, HB, TAIL>(t, acc, v0, lim, gate);
   st[HB * 64] = stats_pack(t);
-  if constexpr (HB + 1 < kGemmHB) fold_all<HB + 1>(st, acc, v0, lim, gate);
+  if constexpr (HB + 1 < G::HB) fold_all<G, HB + 1, TAIL>(st, acc, v0, lim, gate);
 }
 
-__global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs a) {
+// TAIL: V is not a multiple of the tile, so the last tile's padding ids are masked in the fold (a
+// separate instantiation keeps that code out of the common case).
+template <class G, bool TAIL>
+__device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
   // W stage buffers [row * 8 + permuted chunk], one array each so that the compiler can tell a
   // buffer being filled from the one being read (it would otherwise wait for every fill)
-  __shared__ uint4 wring0[kGemmBN * 8], wring1[kGemmBN * 8], wring2[kGemmBN * 8], wring3[kGemmBN * 8];
+  __shared__ uint4 wring0[G::Slot], wring1[G::Slot], wring2[G::Slot], wring3[G::Slot];
   auto ring = [&](int slot) -> uint4* { return slot == 0 ? wring0 : slot == 1 ? wring1 : slot == 2 ? wring2 : wring3; };
+  __shared__ float4 st_lds[kGemmWaves * G::HB * 64];  // running statistics, [wave][hb][lane]
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int rg = blockIdx.x % a.n_rg, gi = blockIdx.x / a.n_rg;
+  // workgroups of one vocabulary range (one per row group) sit 8 block indices apart: one XCD
+  int rg, gi;
+  if ((a.G_t & 7) == 0) {
+    const int q = blockIdx.x >> 3;
+    rg = q % a.n_rg;
+    gi = (q / a.n_rg) * 8 + (blockIdx.x & 7);
+  } else {
+    rg = blockIdx.x % a.n_rg;
+    gi = blockIdx.x / a.n_rg;
+  }
+  rg = __builtin_amdgcn_readfirstlane(rg);                // (uniform; keeps the stage logic scalar)
+  gi = __builtin_amdgcn_readfirstlane(gi);
   const int nt = a.ntiles > gi ? (a.ntiles - gi + a.G_t - 1) / a.G_t : 0;   // tiles gi, gi+G_t, ...
   const int S = a.H / kGemmBK;                            // stages per tile (multiple of 4)
   const int KG = a.H / 16;
-  const int total = nt * S;
+  const int total = __builtin_amdgcn_readfirstlane(nt * S);
   const unsigned row_bytes = (unsigned)a.H * 2u;
   const unsigned kOOB = 0x80000000u;                      // beyond any range: loads return 0
   const __amdgpu_buffer_rsrc_t wrs =
@@ -868,26 +898,29 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
 
   // Addresses split into a per-lane constant (voffset) and a per-stage, wavefront-uniform part
   // (soffset, kOOB past the last stage so the loads return zeros without touching memory).
-  // W load instruction i of this wavefront: tile rows 32w + 8i + l/8, lane l bringing chunk
+  // W load instruction i of this wavefront: tile rows 64w + 8i + l/8, lane l bringing chunk
   // (l%8) ^ swz(row) of the stage's 128-byte segment, landing at LDS slot row * 8 + l%8, with
   // swz(r) = (r ^ (r >> 3)) & 7.
-  unsigned w_voff[kGemmWDma];
+  unsigned w_voff[G::WDma];
 #pragma unroll
-  for (int i = 0; i < kGemmWDma; ++i) {
-    const int r = 32 * wave + 8 * i + (lane >> 3);
+  for (int i = 0; i < G::WDma; ++i) {
+    const int r = 8 * G::WDma * wave + 8 * i + (lane >> 3);
     w_voff[i] = (unsigned)r * row_bytes + 16u * (unsigned)((lane & 7) ^ ((r ^ (r >> 3)) & 7));
   }
   // stage (tile index ti, K block kk) of this workgroup
+  // (readfirstlane: these are wavefront-uniform by construction, and the buffer instructions take
+  // them in scalar registers)
   auto w_soff = [&](int ti, int kk) -> unsigned {
     const int s = ti * S + kk;
-    return s < total ? (unsigned)((gi + ti * a.G_t) * kGemmBN) * row_bytes + (unsigned)(kk * kGemmBK * 2) : kOOB;
+    return __builtin_amdgcn_readfirstlane(
+        s < total ? (unsigned)((gi + ti * a.G_t) * G::BN) * row_bytes + (unsigned)(kk * kGemmBK * 2) : kOOB);
   };
   auto w_issue = [&](int slot, unsigned soff) {
 #pragma unroll
-    for (int i = 0; i < kGemmWDma; ++i)
+    for (int i = 0; i < G::WDma; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          wrs, (__attribute__((address_space(3))) void*)(ring(slot) + (32 * wave + 8 * i) * 8), 16, w_voff[i], soff, 0,
-          0);
+          wrs, (__attribute__((address_space(3))) void*)(ring(slot) + (8 * G::WDma * wave + 8 * i) * 8), 16,
+          w_voff[i], soff, 0, 0);
   };
   // fragment reads: lane l, block vb, K16 step ks reads tile row r = 32vb + l%32, chunk
   // c = 2ks + l/32, at slot r*8 + (c ^ swz(r)) = 256vb + 8(l%32) + (x_l ^ 2(ks ^ 2(vb&1))) with
@@ -900,74 +933,73 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
     return ring(slot)[rd_base[ks ^ (2 * (vb & 1))] + 256 * vb];
   };
   // hidden fragment (block hb, K16 step 4kk + ks) of this wavefront
-  const unsigned h_voff = ((unsigned)(16 * rg + 4 * wave) * (unsigned)KG) * 1024u + 16u * lane;
+  const unsigned h_voff = ((unsigned)((G::Rows / 32) * rg + G::HB * wave) * (unsigned)KG) * 1024u + 16u * lane;
   const unsigned hb_stride = (unsigned)KG * 1024u;        // bytes between 32-row blocks
   auto h_soff = [&](int ti, int kk) -> unsigned {
-    return ti * S + kk < total ? (unsigned)(kk * 4) * 1024u : kOOB;
+    return __builtin_amdgcn_readfirstlane(ti * S + kk < total ? (unsigned)(kk * 4) * 1024u : kOOB);
   };
   auto h_load = [&](unsigned soff, int ks, int hb) -> uint4 {
     return __builtin_bit_cast(
         uint4, __builtin_amdgcn_raw_buffer_load_b128(hrs, h_voff + (unsigned)(ks * 1024), soff + hb * hb_stride, 0));
   };
 
-  uint4 hr[kGemmHDepth][4][kGemmHB], af[2][4];
-  f32x16 acc[4][kGemmHB];
-  __shared__ float4 st_lds[kGemmWaves * kGemmHB * 64];  // running statistics, [wave][hb][lane]
-  float4* const st = st_lds + wave * (kGemmHB * 64) + lane;
+  uint4 hr[G::HDepth][4][G::HB], af[2][G::VB];
+  f32x16 acc[G::VB][G::HB];
+  float4* const st = st_lds + wave * (G::HB * 64) + lane;
 #pragma unroll
-  for (int hb = 0; hb < kGemmHB; ++hb) st[hb * 64] = stats_pack(stats_empty());
+  for (int hb = 0; hb < G::HB; ++hb) st[hb * 64] = stats_pack(stats_empty());
 
-  // prologue: W stages 0..2, hidden stages 0 and 1, then the barrier that opens stage 0.  Every
-  // W load of the prologue has at least kGemmVmAfterW vector-memory instructions behind it by the
-  // barrier that needs it, as in the steady state.  (S >= 4, so stages 0..2 are in tile 0.)
+  // prologue: W stages 0..2, hidden stages 0 .. depth-1, then the barrier that opens stage 0.
+  // Every W load of the prologue has at least G::VmAfterW vector-memory instructions behind it
+  // by the barrier that needs it, as in the steady state.  (S >= 4, so stages 0..2 are in tile 0.)
 #pragma unroll
   for (int p = 0; p < 3; ++p) w_issue(p, w_soff(0, p));
 #pragma unroll
-  for (int p = 0; p < kGemmHDepth; ++p) {
+  for (int p = 0; p < G::HDepth; ++p) {
     const unsigned so = h_soff(0, p);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int hb = 0; hb < kGemmHB; ++hb) hr[p][ks][hb] = h_load(so, ks, hb);
+      for (int hb = 0; hb < G::HB; ++hb) hr[p][ks][hb] = h_load(so, ks, hb);
   }
   __builtin_amdgcn_sched_barrier(0);
-  wait_vmcnt<kGemmVmAfterW>();                            // W stage 0 landed
+  wait_vmcnt<G::VmAfterW>();                            // W stage 0 landed
   __builtin_amdgcn_s_waitcnt(0xc07f);                     // and no LDS access pending
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int vb = 0; vb < 4; ++vb) af[0][vb] = w_frag(0, vb, 0);
+  for (int vb = 0; vb < G::VB; ++vb) af[0][vb] = w_frag(0, vb, 0);
 
   // four stages kk0 .. kk0+3 of tile ti; FIRST: the tile's first group, whose first K16 step
   // starts the accumulators from zero
   auto group = [&](int ti, int kk0, auto first) {
     constexpr bool FIRST = decltype(first)::value;
-    const bool last4 = kk0 + 4 == S;                      // stages kk0+u+2 / +3 may wrap to tile ti+1
+    const bool last4 = kk0 + 4 == S;                      // stages kk0+u+depth / +3 may wrap to tile ti+1
 #pragma unroll
     for (int u = 0; u < 4; ++u) {                         // stage kk0+u: buffer u, hidden set u % depth
-      const int hp = u % kGemmHDepth;
-      const bool hw = last4 && u + kGemmHDepth >= 4, ww = last4 && u + 3 >= 4;
-      const unsigned hso = h_soff(ti + hw, kk0 + u + kGemmHDepth - (hw ? S : 0));
+      const int hp = u % G::HDepth;
+      const bool hw = last4 && u + G::HDepth >= 4, ww = last4 && u + 3 >= 4;
+      const unsigned hso = h_soff(ti + hw, kk0 + u + G::HDepth - (hw ? S : 0));
       const unsigned wso = w_soff(ti + ww, kk0 + u + 3 - (ww ? S : 0));
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int cur = ks & 1, nxt = cur ^ 1;
         if (ks < 3) {
 #pragma unroll
-          for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = w_frag(u, vb, ks + 1);
+          for (int vb = 0; vb < G::VB; ++vb) af[nxt][vb] = w_frag(u, vb, ks + 1);
         }
 #pragma unroll
-        for (int vb = 0; vb < 4; ++vb)
+        for (int vb = 0; vb < G::VB; ++vb)
 #pragma unroll
-          for (int hb = 0; hb < kGemmHB; ++hb)
+          for (int hb = 0; hb < G::HB; ++hb)
             acc[vb][hb] = mma32(af[cur][vb], hr[hp][ks][hb], (FIRST && u == 0 && ks == 0) ? f32x16{} : acc[vb][hb]);
 #pragma unroll
-        for (int hb = 0; hb < kGemmHB; ++hb) hr[hp][ks][hb] = h_load(hso, ks, hb);   // kGemmHDepth stages ahead
+        for (int hb = 0; hb < G::HB; ++hb) hr[hp][ks][hb] = h_load(hso, ks, hb);   // G::HDepth stages ahead
         __builtin_amdgcn_sched_barrier(0);
         if (ks == 1) {
           // open the next stage: its W landed for every wavefront; buffer (u+3)&3 was last read
           // in the previous stage, so the W loads three stages ahead may overwrite it
-          wait_vmcnt<kGemmVmAfterW>();
+          wait_vmcnt<G::VmAfterW>();
           __builtin_amdgcn_s_waitcnt(0xc07f);
           __builtin_amdgcn_s_barrier();
           __builtin_amdgcn_sched_barrier(0);
@@ -976,7 +1008,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
         }
         if (ks == 3) {                                    // next stage's first fragments
 #pragma unroll
-          for (int vb = 0; vb < 4; ++vb) af[nxt][vb] = w_frag((u + 1) & 3, vb, 0);
+          for (int vb = 0; vb < G::VB; ++vb) af[nxt][vb] = w_frag((u + 1) & 3, vb, 0);
         }
       }
     }
@@ -986,17 +1018,17 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
     group(ti, 0, std::true_type{});
     for (int kk0 = 4; kk0 < S; kk0 += 4) group(ti, kk0, std::false_type{});
     // tile done: fold its logits (the next tile's loads are in flight)
-    const int t0 = (gi + ti * a.G_t) * kGemmBN;
+    const int t0 = (gi + ti * a.G_t) * G::BN;
     const int v0 = t0 + 4 * (lane >> 5);
-    fold_all<0>(st, acc, v0, a.V - v0, a.fold_gate);  // ids >= V (last tile) are skipped
+    fold_all<G, 0, TAIL>(st, acc, v0, a.V - v0, a.fold_gate);  // ids >= V are skipped
   }
   __builtin_amdgcn_s_waitcnt(0);                          // no load into LDS may outlive the workgroup
 
   // lanes l and l+32 hold the same rows over different vocabulary ids: merge the pair, then
   // lanes 0..31 write one record per row
-  const unsigned h_row0 = (unsigned)(rg * kGemmRows + wave * kGemmRowsPerWave + (lane & 31));
+  const unsigned h_row0 = (unsigned)(rg * G::Rows + wave * G::RowsPerWave + (lane & 31));
 #pragma unroll
-  for (int hb = 0; hb < kGemmHB; ++hb) {
+  for (int hb = 0; hb < G::HB; ++hb) {
     Stats lo, hi;
     int x0, x1;
     const Stats sh = stats_unpack(st[hb * 64]);
@@ -1010,7 +1042,11 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_stats_kernel(const GemmArgs
   }
 }
 
-// Merge + commit after gemm_stats_kernel: one workgroup per sequence.
+// One kernel per tail handling (plain kernels, so both compilation passes see them)
+__global__ __launch_bounds__(kGemmThreads) void gemm_wide_kernel(const GemmArgs a) { gemm_stats<GemmWide, false>(a); }
+__global__ __launch_bounds__(kGemmThreads) void gemm_wide_tail_kernel(const GemmArgs a) { gemm_stats<GemmWide, true>(a); }
+
+// Merge + commit after the GEMM-path kernel: one workgroup per sequence.
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, const float4* records, int G,
                                                             int nrows_total) {
   __shared__ uint4 stage[kRowsPerStage / 2];
