@@ -114,6 +114,8 @@ typedef struct {
  *   out_commit   [B][L]      uint8    1 where this call fixed the position
  * Every row goes through the LM head; the [B][L][V] logits never reach memory.
  * The workspace carries a completion counter that each call leaves at zero.
+ * hidden and W_vocab must be finite: the kernels are built without NaN handling, so
+ * NaN or Inf inputs give unspecified (but in-bounds, non-faulting) results.
  */
 int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state,
                     dlm_credit_slot* credit_state, const dlm_policy* policy, int32_t* out_tokens,
