@@ -87,7 +87,52 @@ def record_trajectory(wl, W, Wd, steps, dev):
     return hidden, seq, commits, blocks_done
 
 
+def time_steps_device_loop(wl, Wd, hidden, seq, warmup, steps, dev, graph):
+    """All timed steps in one dlm_decode_steps call (optionally captured once as a graph and replayed)."""
+    import torch
+    from decoding_step_amd import _native as nat
+    from decoding_step_amd.device import Decoder, new_credit
+
+    stream = torch.cuda.Stream(dev) if graph else torch.cuda.current_stream(dev)
+    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream)
+    mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
+    credit = new_credit(wl.B, wl.L, dev)
+    credit0 = credit.clone()
+    tok = torch.empty((steps, wl.B, wl.L), dtype=torch.int32, device=dev)
+    com = torch.empty((steps, wl.B, wl.L), dtype=torch.uint8, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(max(1, warmup // max(1, steps))):
+            dec.steps(hidden[:steps], mask, credit, tok, com)
+    torch.cuda.synchronize()
+    run = lambda: dec.steps(hidden[:steps], mask, credit, tok, com)
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        mask.fill_(1)
+        credit.copy_(credit0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=stream):
+            run()
+        run = g.replay
+        stream = torch.cuda.current_stream(dev)
+        dec.policy.set_stream(stream)
+    mask.fill_(1)
+    credit.copy_(credit0)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    with torch.cuda.stream(stream):
+        run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / 1e3, wall, None
+
+
 def time_steps(wl, Wd, hidden, seq, warmup, steps, dev):
+    """One dlm_decode_step call per step.  The region is timed with two events only; a second
+    pass over the same steps records an event between consecutive steps for the per-step
+    distribution (those events add ~3 us to each step, so the rate comes from the first pass)."""
     import torch
     from decoding_step_amd import _native as nat
     from decoding_step_amd.device import Decoder, new_credit
@@ -96,12 +141,17 @@ def time_steps(wl, Wd, hidden, seq, warmup, steps, dev):
     dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream)
     mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
     credit = new_credit(wl.B, wl.L, dev)
+    credit0 = credit.clone()
     for s in range(warmup):                      # warm-up on the first inputs, then reset the state
         dec.step(hidden[s % hidden.shape[0]], mask, credit)
     torch.cuda.synchronize()
-    mask.fill_(1)
-    credit.copy_(new_credit(wl.B, wl.L, dev))
-    torch.cuda.synchronize()
+
+    def reset():
+        mask.fill_(1)
+        credit.copy_(credit0)
+        torch.cuda.synchronize()
+
+    reset()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     start.record(stream)
@@ -110,7 +160,16 @@ def time_steps(wl, Wd, hidden, seq, warmup, steps, dev):
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    return start.elapsed_time(end) / 1e3, wall
+    total = start.elapsed_time(end) / 1e3
+    reset()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for s in range(steps):
+        dec.step(hidden[s], mask, credit)
+        ev[s + 1].record(stream)
+    torch.cuda.synchronize()
+    per_step = [ev[i].elapsed_time(ev[i + 1]) * 1e3 for i in range(steps)]   # us
+    return total, wall, per_step
 
 
 def cpu_baseline(wl, W, budget_s=20.0):
@@ -119,11 +178,8 @@ def cpu_baseline(wl, W, budget_s=20.0):
     import oracle
     from decoding_step_amd.synth import BlockStream
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     seq = [(p.kind, p.threshold, p.decay, p.max_depth) for p in wl.policies]
     streams = [BlockStream(W, wl.L, s, wl.a_max, rp) for s, rp in zip(wl.seeds, wl.redraw_p)]
     mask = np.ones((wl.B, wl.L), np.uint8)
@@ -140,8 +196,22 @@ def cpu_baseline(wl, W, budget_s=20.0):
         for b in range(wl.B):
             pos[b] = [pos[b][0] + 1, 0] if not mask[b].any() else [pos[b][0], pos[b][1] + 1]
         n += 1
+    # the same oracle on one thread, on the first step only
+    h = np.stack([BlockStream(W, wl.L, sd, wl.a_max, rp).hidden(0, 0) for sd, rp in zip(wl.seeds, wl.redraw_p)])
+    with threadpool_limits(limits=1, user_api="blas"):
+        t1 = time.perf_counter()
+        oracle.decode_step(h, W, np.ones((wl.B, wl.L), np.uint8), seq, np.full((wl.B, wl.L, 4), -1, np.int32),
+                           np.zeros((wl.B, wl.L, 4), np.float32), auto_advance=True)
+        t1 = time.perf_counter() - t1
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), "")
+    except OSError:  # pragma: no cover
+        pass
     return {"value": wl.B * wl.L * n / t, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} steps of {wl.name} (whole steps, all {wl.B * wl.L} rows), {t:.1f} s"}
+            "sample": f"first {n} steps of {wl.name} (whole steps, all {wl.B * wl.L} rows), {t:.1f} s",
+            "one_thread_value": wl.B * wl.L / t1, "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": model}
 
 
 def main():
@@ -151,6 +221,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="threshold_b1_l32")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--loop", choices=["calls", "steps", "graph"], default="calls",
+                    help="one dlm_decode_step call per step (default), all timed steps in one "
+                         "dlm_decode_steps call, or that call captured as a graph and replayed")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -158,6 +231,7 @@ def main():
               "(the step shards by sequence or by vocabulary range; see the design notes).", file=sys.stderr)
         sys.exit(2)
 
+    import numpy as np
     import torch
     from decoding_step_amd import _native as nat
     from decoding_step_amd.device import to_device
@@ -177,7 +251,11 @@ def main():
     print(f"[bench] recording {n_in} steps", file=sys.stderr, flush=True)
     hidden, seq, commits, blocks = record_trajectory(wl, W, Wd, n_in, dev)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
-    t, wall = time_steps(wl, Wd, hidden, seq, args.warmup, args.steps, dev)
+    if args.loop == "calls":
+        t, wall, per_step = time_steps(wl, Wd, hidden, seq, args.warmup, args.steps, dev)
+    else:
+        t, wall, per_step = time_steps_device_loop(wl, Wd, hidden, seq, args.warmup, args.steps, dev,
+                                                   graph=args.loop == "graph")
     ms = t / args.steps * 1e3
     bytes_, flops = algorithmic_work(wl)
     sec_per_step = t / args.steps
@@ -203,7 +281,13 @@ def main():
                    "policies": sorted(set(f"{['threshold', 'hierarchical', 'credit'][p.kind]} {p.threshold}"
                                           for p in wl.policies))},
         "roofline": roof,
+        "step_us": None if per_step is None else {
+            "median": float(np.median(per_step)), "p10": float(np.percentile(per_step, 10)),
+            "p90": float(np.percentile(per_step, 90)),
+            "note": "second pass with an event between steps (each event adds ~3 us)"},
+        "loop": args.loop,
         "committed_tok_per_s": commits / args.steps / sec_per_step,
+        "per_sequence_tok_per_s": commits / args.steps / sec_per_step / wl.B,
         "blocks_completed": blocks,
         "host_wall_s": wall,
     }

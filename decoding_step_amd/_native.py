@@ -65,6 +65,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     pol = ctypes.POINTER(dlm_policy)
     lib.dlm_decode_step.argtypes = [vp, vp, vp, vp, pol, vp, vp]
     lib.dlm_decode_step.restype = ctypes.c_int
+    lib.dlm_decode_steps.argtypes = [vp, vp, vp, vp, pol, i64, vp, vp]
+    lib.dlm_decode_steps.restype = ctypes.c_int
     lib.dlm_token_stats.argtypes = [vp, vp, pol, vp, vp, vp]
     lib.dlm_token_stats.restype = ctypes.c_int
     lib.dlm_commit.argtypes = [vp, vp, vp, vp, pol, vp]
@@ -145,6 +147,13 @@ class StepPolicy:
 def dlm_decode_step(hidden, W_vocab, mask_state, credit_state, policy: StepPolicy, out_tokens, out_commit) -> None:
     _check(load().dlm_decode_step(_ptr(hidden), _ptr(W_vocab), _ptr(mask_state), _ptr(credit_state),
                                   ctypes.byref(policy.c), _ptr(out_tokens), _ptr(out_commit)))
+
+
+def dlm_decode_steps(hidden_steps, W_vocab, mask_state, credit_state, policy: StepPolicy, n_steps: int,
+                     out_tokens_steps, out_commit_steps) -> None:
+    _check(load().dlm_decode_steps(_ptr(hidden_steps), _ptr(W_vocab), _ptr(mask_state), _ptr(credit_state),
+                                   ctypes.byref(policy.c), int(n_steps), _ptr(out_tokens_steps),
+                                   _ptr(out_commit_steps)))
 
 
 def dlm_token_stats(hidden, W_vocab, policy: StepPolicy, out_conf, out_tokens, out_gap=None) -> None:

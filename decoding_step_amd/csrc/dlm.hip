@@ -260,6 +260,37 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
   return run_step(hidden, W_vocab, policy, c, true);
 }
 
+int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mask_state,
+                     dlm_credit_slot* credit_state, const dlm_policy* policy, int64_t n_steps,
+                     int32_t* out_tokens_steps, uint8_t* out_commit_steps) {
+  if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");
+  if (!hidden_steps || !W_vocab || !mask_state || !out_tokens_steps || !out_commit_steps)
+    return fail(DLM_ERR_NULL, "hidden_steps, W_vocab, mask_state, out_tokens_steps and out_commit_steps must be non-NULL");
+  if (n_steps < 1) return fail(DLM_ERR_SHAPE, "n_steps=%lld must be >= 1", (long long)n_steps);
+  dlm::CommitArgs c;
+  std::memset(&c, 0, sizeof c);
+  Plan p;
+  int rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, &p);
+  if (rc) return rc;
+  rc = pack_rules(policy, true, credit_state, &c);
+  if (rc) return rc;
+  const size_t rows = (size_t)(policy->B * policy->L);
+  const size_t step_bytes = rows * (size_t)policy->H * (size_t)elem_bytes(policy->dtype);
+  if (misaligned(hidden_steps, 16) || step_bytes % 16)
+    return fail(DLM_ERR_SHAPE, "hidden_steps must be 16-byte aligned (and so every step's slice)");
+  c.mask = mask_state;
+  c.credit = credit_state;
+  c.out_conf = policy->out_conf;
+  c.out_gap = policy->out_gap;
+  for (int64_t n = 0; n < n_steps; ++n) {
+    c.out_tokens = out_tokens_steps + n * rows;
+    c.out_commit = out_commit_steps + n * rows;
+    rc = run_step(static_cast<const char*>(hidden_steps) + n * step_bytes, W_vocab, policy, c, true);
+    if (rc) return rc;  // only a failed launch can get here, after validation passed
+  }
+  return ok();
+}
+
 int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* policy, float* out_conf,
                     int32_t* out_tokens, float* out_gap) {
   if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");

@@ -66,5 +66,11 @@ class Decoder:
     def step(self, hidden: torch.Tensor, mask: torch.Tensor, credit=None) -> None:
         nat.dlm_decode_step(hidden, self.W, mask, credit, self.policy, self.out_tokens, self.out_commit)
 
+    def steps(self, hidden_steps: torch.Tensor, mask: torch.Tensor, credit, out_tokens: torch.Tensor,
+              out_commit: torch.Tensor) -> None:
+        """hidden_steps[n] for step n; per-step outputs [n][B][L] (dlm_decode_steps)."""
+        nat.dlm_decode_steps(hidden_steps, self.W, mask, credit, self.policy, hidden_steps.shape[0], out_tokens,
+                             out_commit)
+
     def token_stats(self, hidden: torch.Tensor, conf: torch.Tensor, tokens: torch.Tensor, gap=None) -> None:
         nat.dlm_token_stats(hidden, self.W, self.policy, conf, tokens, gap)

@@ -122,6 +122,26 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
                     uint8_t* out_commit);
 
 /*
+ * N decode steps enqueued back to back on policy->stream with no host work between them: the
+ * iterations of a block run device-resident (the explainer's system-level optimisations remove
+ * the idle time between diffusion iterations).  Step n reads hidden_steps[n], the hidden states
+ * staged for that iteration, and writes out_tokens_steps[n] / out_commit_steps[n]; mask_state
+ * and credit_state carry over on the device from one step to the next, and with
+ * DLM_AUTO_ADVANCE a sequence whose block completed starts the next block in the following
+ * step.  The result equals n_steps calls of dlm_decode_step.
+ *   hidden_steps      [n_steps][B][L][H]  dtype
+ *   out_tokens_steps  [n_steps][B][L]     int32
+ *   out_commit_steps  [n_steps][B][L]     uint8
+ *   n_steps           >= 1 (DLM_ERR_SHAPE otherwise)
+ * policy->out_conf / out_gap, if set, hold the last step's values.  Everything is validated
+ * before the first launch; on error nothing is enqueued.  The call allocates nothing, waits for
+ * nothing and records no memset, so it may be captured into a HIP graph and replayed.
+ */
+int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mask_state,
+                     dlm_credit_slot* credit_state, const dlm_policy* policy, int64_t n_steps,
+                     int32_t* out_tokens_steps, uint8_t* out_commit_steps);
+
+/*
  * LM head + per-row statistics only (no commit): for every row, the
  * confidence, the candidate token and the top-2 logit gap.  policy->seq,
  * flags, out_conf and out_gap are ignored; out_gap may be NULL.

@@ -157,6 +157,24 @@ def test_token_stats_and_commit_validation():
     assert status_of(nat.dlm_workspace_init, None, 16) == nat.DLM_ERR_NULL
 
 
+def test_decode_steps_validation():
+    # every check of dlm_decode_step, plus the step count, before anything is enqueued
+    need = nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_BF16)
+    p = policy(ws_bytes=need)
+    steps = lambda pol, n=2, hidden=FAKE, tok=FAKE, com=FAKE: status_of(
+        nat.dlm_decode_steps, hidden, FAKE, FAKE, FAKE, pol, n, tok, com)
+    assert steps(p, n=0) == nat.DLM_ERR_SHAPE
+    assert steps(p, n=-3) == nat.DLM_ERR_SHAPE
+    assert steps(p, hidden=None) == nat.DLM_ERR_NULL
+    assert steps(p, tok=None) == nat.DLM_ERR_NULL
+    assert steps(p, com=None) == nat.DLM_ERR_NULL
+    assert steps(p, hidden=MISALIGNED) == nat.DLM_ERR_SHAPE
+    assert steps(policy(ws_bytes=need - 1)) == nat.DLM_ERR_WORKSPACE
+    assert steps(policy(L=65)) == nat.DLM_ERR_SHAPE
+    assert steps(policy(seq=[(7, 0.9, 0, 0)])) == nat.DLM_ERR_POLICY
+    assert nat.load().dlm_decode_steps(FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, FAKE) == nat.DLM_ERR_NULL
+
+
 def test_binding_raises_without_library(tmp_path):
     saved = nat._lib
     try:
