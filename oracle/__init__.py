@@ -11,5 +11,6 @@ from .reference import (  # noqa: F401
     THRESHOLD, HIERARCHICAL, CREDIT, SLOTS,
     as_f64, lm_head_logits, token_stats,
     commit_threshold, commit_hierarchical, commit_credit,
+    RUNNING, FINISHED, EOS_IN_BLOCK, early_stop,
     decode_step,
 )

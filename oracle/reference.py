@@ -262,17 +262,51 @@ def commit_credit(conf: np.ndarray, tok: np.ndarray, mask: np.ndarray,
 # The whole step
 # --------------------------------------------------------------------------------------------
 def _policy_fields(p) -> tuple:
+    """(kind, threshold, decay, max_depth, eos_token); eos_token -1 = no end token."""
     if isinstance(p, dict):
-        return int(p["kind"]), float(p["threshold"]), float(p.get("decay", 0.0)), int(p.get("max_depth", 0))
+        return (int(p["kind"]), float(p["threshold"]), float(p.get("decay", 0.0)), int(p.get("max_depth", 0)),
+                int(p.get("eos_token", -1)))
     if hasattr(p, "kind"):
-        return int(p.kind), float(p.threshold), float(getattr(p, "decay", 0.0)), int(getattr(p, "max_depth", 0))
-    kind, thr, dec, depth = p
-    return int(kind), float(thr), float(dec), int(depth)
+        return (int(p.kind), float(p.threshold), float(getattr(p, "decay", 0.0)), int(getattr(p, "max_depth", 0)),
+                int(getattr(p, "eos_token", -1)))
+    kind, thr, dec, depth = p[:4]
+    return int(kind), float(thr), float(dec), int(depth), int(p[4]) if len(p) > 4 else -1
+
+
+# Early stop (the explainer's engineering paragraph: once an end token appears in the generated
+# text, the computation that would follow it is skipped).  Per sequence, an optional state:
+RUNNING, FINISHED, EOS_IN_BLOCK = 0, 1, 2
+
+
+def early_stop(commit: np.ndarray, tok: np.ndarray, mask_after: np.ndarray, eos: int, state: int):
+    """Apply one step's end-token rule to one sequence (readings E2, E3).
+
+    ``commit`` is the policy's commit set, ``mask_after`` the mask with those commits removed.
+    When the step commits the end token, the text ends at the first such position e: every
+    position after e that is still masked is committed too, and every position after e that
+    this step commits (by the policy or as padding) carries the end token.  The state becomes
+    EOS_IN_BLOCK, and FINISHED once the block has no masked position left.
+    Returns (commit, tokens, mask_after, state) as new arrays.
+    """
+    commit, tok, mask_after = commit.copy(), tok.copy(), mask_after.copy()
+    ends = [l for l in range(len(commit)) if commit[l] and tok[l] == eos]
+    if ends:
+        e = ends[0]
+        for p in range(e + 1, len(commit)):
+            if mask_after[p] or commit[p]:
+                commit[p] = True
+                tok[p] = eos
+                mask_after[p] = False
+        state = EOS_IN_BLOCK
+    if state == EOS_IN_BLOCK and not mask_after.any():
+        state = FINISHED
+    return commit, tok, mask_after, state
 
 
 def decode_step(hidden: np.ndarray, W: np.ndarray, mask: np.ndarray, policies: Iterable,
                 credit_tok: np.ndarray | None = None, credit_val: np.ndarray | None = None,
-                auto_advance: bool = False, stats: dict | None = None) -> dict:
+                auto_advance: bool = False, stats: dict | None = None,
+                seq_done: np.ndarray | None = None) -> dict:
     """One decode step over ``B`` sequences of ``L`` positions.
 
     ``hidden`` ``[B][L][H]``, ``W`` ``[V][H]`` (uint16 bf16 bits or float32),
@@ -284,8 +318,14 @@ def decode_step(hidden: np.ndarray, W: np.ndarray, mask: np.ndarray, policies: I
     iteration manager moves to the next fixed-size block.  ``stats`` may pass
     precomputed :func:`token_stats` output.
 
-    Returns new arrays: ``tokens`` (candidate of every row, R17), ``commit``,
-    ``mask``, ``credit_tok``, ``credit_val``, ``conf``, ``gap``, ``score``.
+    ``seq_done`` (``[B]``, RUNNING / FINISHED / EOS_IN_BLOCK) turns on early stop for the
+    sequences whose policy names an end token (readings E1-E4): a FINISHED sequence commits
+    nothing and keeps its state (no block advance either); otherwise :func:`early_stop` runs
+    after the policy; a new block resets EOS_IN_BLOCK to RUNNING.
+
+    Returns new arrays: ``tokens`` (candidate of every row, R17, or the end token where a
+    position was padded after it), ``commit``, ``mask``, ``credit_tok``, ``credit_val``,
+    ``conf``, ``gap``, ``score``, and ``seq_done`` when given.
     """
     hidden = np.asarray(hidden)
     B, L = hidden.shape[0], hidden.shape[1]
@@ -302,11 +342,18 @@ def decode_step(hidden: np.ndarray, W: np.ndarray, mask: np.ndarray, policies: I
         cval = np.array(credit_val, dtype=np.float32, copy=True).reshape(B, L, SLOTS)
     commit = np.zeros((B, L), dtype=bool)
     score = np.full((B, L), -np.inf, dtype=np.float32)
-    for b, (kind, thr, dec, depth) in enumerate(policies):
+    tok = tok.astype(np.int32).copy()
+    done = None if seq_done is None else np.array(seq_done, dtype=np.uint8, copy=True).reshape(B)
+    for b, (kind, thr, dec, depth, eos) in enumerate(policies):
+        stopping = done is not None and eos >= 0
+        if stopping and done[b] == FINISHED:
+            continue                                  # E1: nothing more for this sequence
         if auto_advance and not new_mask[b].any():
             new_mask[b] = True
             ctok[b] = EMPTY
             cval[b] = 0.0
+            if stopping:
+                done[b] = RUNNING
         if kind == THRESHOLD:
             commit[b] = commit_threshold(conf[b], new_mask[b], thr)
         elif kind == HIERARCHICAL:
@@ -317,7 +364,9 @@ def decode_step(hidden: np.ndarray, W: np.ndarray, mask: np.ndarray, policies: I
         else:
             raise ValueError(f"unknown policy kind {kind}")
         new_mask[b] &= ~commit[b]
-    return {
+        if stopping:
+            commit[b], tok[b], new_mask[b], done[b] = early_stop(commit[b], tok[b], new_mask[b], eos, int(done[b]))
+    out = {
         "tokens": tok.astype(np.int32),
         "commit": commit.astype(np.uint8),
         "mask": new_mask.astype(np.uint8),
@@ -327,3 +376,6 @@ def decode_step(hidden: np.ndarray, W: np.ndarray, mask: np.ndarray, policies: I
         "gap": gap.astype(np.float32),
         "score": score,
     }
+    if done is not None:
+        out["seq_done"] = done
+    return out
