@@ -20,6 +20,7 @@ DLM_OK, DLM_ERR_NULL, DLM_ERR_DTYPE, DLM_ERR_SHAPE, DLM_ERR_POLICY, DLM_ERR_WORK
 DLM_F32, DLM_BF16 = 0, 1
 DLM_THRESHOLD, DLM_HIERARCHICAL, DLM_CREDIT = 0, 1, 2
 DLM_AUTO_ADVANCE = 1
+DLM_SEQ_RUNNING, DLM_SEQ_FINISHED, DLM_SEQ_EOS_IN_BLOCK = 0, 1, 2
 DLM_MAX_SEQS, DLM_MAX_L, DLM_CREDIT_SLOTS, DLM_MAX_RULES = 256, 64, 4, 8
 
 STATUS_NAMES = {0: "DLM_OK", -1: "DLM_ERR_NULL", -2: "DLM_ERR_DTYPE", -3: "DLM_ERR_SHAPE",
@@ -32,7 +33,7 @@ class dlm_credit_slot(ctypes.Structure):
 
 class dlm_seq_policy(ctypes.Structure):
     _fields_ = [("kind", ctypes.c_int32), ("threshold", ctypes.c_float),
-                ("decay", ctypes.c_float), ("max_depth", ctypes.c_int32)]
+                ("decay", ctypes.c_float), ("max_depth", ctypes.c_int32), ("eos_token", ctypes.c_int32)]
 
 
 class dlm_policy(ctypes.Structure):
@@ -41,7 +42,8 @@ class dlm_policy(ctypes.Structure):
                 ("seq", ctypes.POINTER(dlm_seq_policy)),
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("stream", ctypes.c_void_p),
-                ("out_conf", ctypes.c_void_p), ("out_gap", ctypes.c_void_p)]
+                ("out_conf", ctypes.c_void_p), ("out_gap", ctypes.c_void_p),
+                ("seq_done", ctypes.c_void_p)]
 
 
 class DlmError(RuntimeError):
@@ -107,20 +109,23 @@ def _stream_handle(stream) -> Optional[int]:
 class StepPolicy:
     """Python side of ``dlm_policy``: shapes, per-sequence rules and launch context.
 
-    ``seq`` is a list of ``(kind, threshold, decay, max_depth)`` tuples or
-    objects with those fields.  The C struct is built once and reused; only
-    pointers change between calls.
+    ``seq`` is a list of ``(kind, threshold, decay, max_depth[, eos_token])``
+    tuples or objects with those fields (``eos_token`` -1 when absent).  The C
+    struct is built once and reused; only pointers change between calls.
     """
 
     def __init__(self, B: int, L: int, H: int, V: int, dtype: int, seq: Sequence, workspace=None,
-                 workspace_bytes: Optional[int] = None, flags: int = 0, stream=None, out_conf=None, out_gap=None):
+                 workspace_bytes: Optional[int] = None, flags: int = 0, stream=None, out_conf=None, out_gap=None,
+                 seq_done=None):
         self._seq = (dlm_seq_policy * max(1, len(seq)))()
         for i, s in enumerate(seq):
             if hasattr(s, "kind"):
                 k, t, d, m = s.kind, s.threshold, getattr(s, "decay", 0.0), getattr(s, "max_depth", 0)
+                e = getattr(s, "eos_token", -1)
             else:
-                k, t, d, m = s
-            self._seq[i] = dlm_seq_policy(int(k), float(t), float(d), int(m))
+                k, t, d, m = s[:4]
+                e = s[4] if len(s) > 4 else -1
+            self._seq[i] = dlm_seq_policy(int(k), float(t), float(d), int(m), int(e))
         self.c = dlm_policy()
         self.c.B, self.c.L, self.c.H, self.c.V, self.c.dtype, self.c.flags = B, L, H, V, dtype, flags
         self.c.seq = ctypes.cast(self._seq, ctypes.POINTER(dlm_seq_policy)) if len(seq) else None
@@ -128,7 +133,8 @@ class StepPolicy:
         self.c.stream = _stream_handle(stream)
         self.c.out_conf = _ptr(out_conf)
         self.c.out_gap = _ptr(out_gap)
-        self._keep = (workspace, out_conf, out_gap)
+        self.c.seq_done = _ptr(seq_done)
+        self._keep = (workspace, out_conf, out_gap, seq_done)
 
     def set_workspace(self, workspace, nbytes: Optional[int] = None) -> None:
         self.c.workspace = _ptr(workspace)
@@ -138,6 +144,9 @@ class StepPolicy:
 
     def set_stream(self, stream) -> None:
         self.c.stream = _stream_handle(stream)
+
+    def set_seq_done(self, seq_done=None) -> None:
+        self.c.seq_done = _ptr(seq_done)
 
     def set_outputs(self, out_conf=None, out_gap=None) -> None:
         self.c.out_conf = _ptr(out_conf)

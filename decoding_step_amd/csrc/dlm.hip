@@ -12,6 +12,9 @@
 #include "dlm.h"
 #include "dlm_device.hpp"
 
+static_assert(sizeof(dlm_seq_policy) == 20 && sizeof(dlm_policy) == 96 && sizeof(dlm_credit_slot) == 8,
+              "C ABI struct layout (the Python binding mirrors it)");
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -118,8 +121,10 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
 bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
 // Validate the per-sequence rules and pack them (distinct rules + index per sequence).
-int pack_rules(const dlm_policy* pol, bool need_credit_state, const void* credit, dlm::CommitArgs* c) {
+// vocab: the vocabulary size the end tokens must fall in (0: not known to this call).
+int pack_rules(const dlm_policy* pol, bool need_credit_state, const void* credit, int64_t vocab, dlm::CommitArgs* c) {
   if (!pol->seq) return fail(DLM_ERR_NULL, "policy->seq is NULL");
+  c->seq_done = pol->seq_done;
   int n = 0;
   bool any_credit = false;
   for (int64_t b = 0; b < pol->B; ++b) {
@@ -132,12 +137,16 @@ int pack_rules(const dlm_policy* pol, bool need_credit_state, const void* credit
       return fail(DLM_ERR_POLICY, "seq[%lld].decay=%g outside [0, 1)", (long long)b, (double)s.decay);
     if (s.kind == DLM_HIERARCHICAL && s.max_depth < 0)
       return fail(DLM_ERR_POLICY, "seq[%lld].max_depth=%d is negative", (long long)b, (int)s.max_depth);
+    if (s.eos_token < -1 || (vocab > 0 && s.eos_token >= vocab))
+      return fail(DLM_ERR_POLICY, "seq[%lld].eos_token=%d is neither -1 nor a token id", (long long)b,
+                  (int)s.eos_token);
     any_credit |= s.kind == DLM_CREDIT;
     dlm::Rule r;
     r.kind = s.kind;
     r.thr = s.threshold;
     r.decay = s.kind == DLM_CREDIT ? s.decay : 0.f;
     r.depth = s.kind == DLM_HIERARCHICAL ? s.max_depth : 0;
+    r.eos = pol->seq_done ? s.eos_token : -1;
     int k = 0;
     for (; k < n; ++k)
       if (std::memcmp(&c->rules[k], &r, sizeof r) == 0) break;
@@ -249,7 +258,7 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
   Plan p;
   int rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, &p);
   if (rc) return rc;
-  rc = pack_rules(policy, true, credit_state, &c);
+  rc = pack_rules(policy, true, credit_state, policy->V, &c);
   if (rc) return rc;
   c.mask = mask_state;
   c.credit = credit_state;
@@ -272,7 +281,7 @@ int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mas
   Plan p;
   int rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, &p);
   if (rc) return rc;
-  rc = pack_rules(policy, true, credit_state, &c);
+  rc = pack_rules(policy, true, credit_state, policy->V, &c);
   if (rc) return rc;
   const size_t rows = (size_t)(policy->B * policy->L);
   const size_t step_bytes = rows * (size_t)policy->H * (size_t)elem_bytes(policy->dtype);
@@ -315,7 +324,7 @@ int dlm_commit(const float* conf, const int32_t* tokens, uint8_t* mask_state, dl
     return fail(DLM_ERR_SHAPE, "L=%lld outside [1, %d]", (long long)policy->L, DLM_MAX_L);
   dlm::CommitArgs c;
   std::memset(&c, 0, sizeof c);
-  int rc = pack_rules(policy, true, credit_state, &c);
+  int rc = pack_rules(policy, true, credit_state, 0, &c);
   if (rc) return rc;
   c.mask = mask_state;
   c.credit = credit_state;

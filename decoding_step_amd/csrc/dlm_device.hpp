@@ -36,6 +36,7 @@ struct Rule {
   float thr;
   float decay;
   int depth;
+  int eos;   // end token for early stop, -1 = none (also when the call has no state array)
 };
 
 // Everything the commit policies touch.
@@ -46,6 +47,7 @@ struct CommitArgs {
   uint8_t* out_commit;
   float* out_conf;
   float* out_gap;
+  uint8_t* seq_done;   // [B] early-stop state (DLM_SEQ_*), or null
   int B, L;
   unsigned flags;
   Rule rules[DLM_MAX_RULES];
@@ -364,12 +366,24 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
   const Rule R = a.rules[a.rule_of[b]];
   if (!in) conf = -INFINITY;
 
+  // early stop: a finished sequence only reports its candidates (its state stays as it is)
+  const bool stopping = R.eos >= 0;
+  int done = stopping ? (int)a.seq_done[b] : DLM_SEQ_RUNNING;
+  if (done == DLM_SEQ_FINISHED) {
+    if (in) {
+      if (a.out_tokens) a.out_tokens[row] = tok;
+      a.out_commit[row] = 0;
+    }
+    return;
+  }
+
   bool masked = in_state.masked;
   uint64_t U = ballot(masked);
   const bool advance = U == 0ull && (a.flags & DLM_AUTO_ADVANCE);
   if (advance) {
     masked = in;
     U = ballot(masked);
+    done = DLM_SEQ_RUNNING;
   }
 
   // credit slots of this position (cleared when a new block starts)
@@ -431,9 +445,26 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
     if (C == 0ull && U != 0ull) C = 1ull << argmax_lane(masked ? score : -INFINITY);
   }
 
+  // early stop: when the end token commits, the text ends at its first position e; every
+  // position after e still masked commits too, and every position after e committed now
+  // carries the end token.  The block that completes after it finishes the sequence.
+  uint64_t pad = 0;
+  if (stopping) {
+    const uint64_t E = ballot(((C >> l) & 1ull) && tok == R.eos);
+    if (E != 0ull) {
+      const int e = __builtin_ctzll(E);
+      const uint64_t after = e >= 63 ? 0ull : (~0ull << (e + 1));
+      C |= U & after;
+      pad = C & after;
+      done = DLM_SEQ_EOS_IN_BLOCK;
+    }
+    if (done == DLM_SEQ_EOS_IN_BLOCK && (U & ~C) == 0ull) done = DLM_SEQ_FINISHED;
+    if (l == 0) a.seq_done[b] = (uint8_t)done;
+  }
+
   if (in) {
     const bool c = (C >> l) & 1ull;
-    if (a.out_tokens) a.out_tokens[row] = tok;
+    if (a.out_tokens) a.out_tokens[row] = ((pad >> l) & 1ull) ? R.eos : tok;
     a.out_commit[row] = c ? 1 : 0;
     a.mask[row] = (masked && !c) ? 1 : 0;
     if (has_credit && (advance || (masked && R.kind == DLM_CREDIT))) {

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DLM_VERSION_STRING "0.1.0"
+#define DLM_VERSION_STRING "0.2.0"
 
 #define DLM_MAX_SEQS 256   /* sequences per call                                  */
 #define DLM_MAX_L 64       /* positions per block: one wavefront lane per position */
@@ -83,7 +83,24 @@ typedef struct {
   float threshold;   /* threshold, hierarchical: tau on conf; credit: theta on score     */
   float decay;       /* credit only: per-iteration credit factor, 0 <= decay < 1          */
   int32_t max_depth; /* hierarchical only: split depth limit, 0 = unbounded (runs = 1)    */
+  int32_t eos_token; /* end token for early stop (needs dlm_policy.seq_done), -1 = none  */
 } dlm_seq_policy;
+
+/*
+ * Early stop on the end token (explainer, engineering paragraph: once an end token appears in
+ * the generated text the computation that would follow it is skipped).  With
+ * dlm_policy.seq_done set, a sequence whose rule names an end token keeps a state:
+ *   DLM_SEQ_RUNNING       decoding;
+ *   DLM_SEQ_EOS_IN_BLOCK  the end token was committed in the current block;
+ *   DLM_SEQ_FINISHED      the block containing the end token is complete: the sequence commits
+ *                         nothing more, its mask and credit stay as they are and
+ *                         DLM_AUTO_ADVANCE starts no new block for it (the caller resets the
+ *                         state to reuse the slot).
+ * A step that commits the end token also commits every still-masked position after the first
+ * such position, and every position after it committed by that step carries the end token
+ * (dlm_decode_step reports it in out_tokens; dlm_commit's caller applies it to its tokens).
+ */
+enum { DLM_SEQ_RUNNING = 0, DLM_SEQ_FINISHED = 1, DLM_SEQ_EOS_IN_BLOCK = 2 };
 
 /* Shapes, per-sequence rules and launch context of one call. */
 typedef struct {
@@ -99,6 +116,8 @@ typedef struct {
   void* stream;              /* hipStream_t                                                */
   float* out_conf;           /* optional device [B][L]: confidence of every row, or NULL   */
   float* out_gap;            /* optional device [B][L]: top-1 minus top-2 logit, or NULL   */
+  uint8_t* seq_done;         /* optional device [B], in/out: early-stop state (DLM_SEQ_*);
+                                NULL disables early stop for every sequence                 */
 } dlm_policy;
 
 /*

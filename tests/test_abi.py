@@ -46,9 +46,11 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ["DLM_MAX_SEQS", "DLM_MAX_L", "DLM_CREDIT_SLOTS", "DLM_MAX_RULES"]:
         assert int(re.search(rf"#define {name} (\d+)", text).group(1)) == getattr(nat, name)
+    for name in ["DLM_SEQ_RUNNING", "DLM_SEQ_FINISHED", "DLM_SEQ_EOS_IN_BLOCK"]:
+        assert int(re.search(rf"{name} = (\d+)", text).group(1)) == getattr(nat, name)
     assert ctypes.sizeof(nat.dlm_credit_slot) == 8
-    assert ctypes.sizeof(nat.dlm_seq_policy) == 16
-    assert ctypes.sizeof(nat.dlm_policy) == 88
+    assert ctypes.sizeof(nat.dlm_seq_policy) == 20       # the library asserts the same sizes
+    assert ctypes.sizeof(nat.dlm_policy) == 96
 
 
 def test_workspace_sizes():
@@ -123,6 +125,19 @@ def test_bad_shapes(kw):
 ])
 def test_bad_policies(seq):
     assert step(policy(seq=seq)) == nat.DLM_ERR_POLICY
+
+
+def test_bad_end_tokens():
+    assert step(policy_with_done(V=1024, eos=-2)) == nat.DLM_ERR_POLICY
+    assert step(policy_with_done(V=1024, eos=1024)) == nat.DLM_ERR_POLICY
+    # dlm_commit knows no vocabulary: any token id >= 0 passes, -2 does not
+    p = policy_with_done(V=1024, eos=-2)
+    assert status_of(nat.dlm_commit, FAKE, FAKE, FAKE, FAKE, p, FAKE) == nat.DLM_ERR_POLICY
+
+
+def policy_with_done(V, eos):
+    return nat.StepPolicy(1, 8, 64, V, nat.DLM_BF16, [(nat.DLM_THRESHOLD, 0.9, 0.0, 0, eos)], workspace=FAKE,
+                          workspace_bytes=1 << 20, seq_done=FAKE)
 
 
 def test_too_many_distinct_rules():
