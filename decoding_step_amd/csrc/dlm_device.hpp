@@ -20,7 +20,7 @@ namespace dlm {
 constexpr int kWaves = 8;             // wavefronts per workgroup
 constexpr int kThreads = kWaves * 64; // workgroup size
 constexpr int kTileRows = 16;         // vocabulary rows per MFMA tile
-constexpr int kPrefetch = 16;         // 16-byte W fragments in flight per lane
+constexpr int kPrefetch = 8;          // 16-byte W fragments in flight per lane (measured: 8 beats 16 and 32)
 constexpr int kRowsPerStage = 1024;   // finalize: rows staged in LDS at a time
 constexpr int kRowBatch = 4;          // finalize: rows per wavefront with loads in flight together
 constexpr int kMaxVocabGroups = 256;  // vocabulary ranges (records per row) at most
