@@ -518,7 +518,9 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
         const Stats t = merge_records(row_stats);
         if (rr < nrows && lane == 0) {
           const int row = r_first + rr;
-          const float conf = 1.f / t.s;
+          // S >= 1 in exact arithmetic (the top logit's own term is 1); the exponent of that
+          // term carries the rounding of m*log2(e), so 1/S may land a few ulps above 1
+          const float conf = fminf(1.f / t.s, 1.f);
           s_conf[rr] = conf;
           s_tok[rr] = t.id;
           if (c.out_conf) c.out_conf[row] = conf;

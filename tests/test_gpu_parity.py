@@ -164,6 +164,7 @@ def test_token_stats_against_oracle(B, L, H, V, dtype):
     sure = ref["gap"] >= 1e-2
     np.testing.assert_array_equal(tok[sure], ref["tok"][sure])
     np.testing.assert_allclose(conf, ref["conf"], rtol=1e-3)
+    assert np.all(conf <= 1.0) and np.all(conf > 0.0)       # the largest probability lies in (0, 1]
     fin = np.isfinite(ref["gap"])
     np.testing.assert_allclose(gap[fin], ref["gap"][fin], rtol=1e-3, atol=2e-3)
     assert np.all(np.isinf(gap[~fin]))
