@@ -37,7 +37,8 @@ updated before it is tested (R9); decay-then-add (R10); a candidate not in a
 slot evicts the first empty slot, else the smallest credit, lowest slot on
 ties (R11); the committed token is the current arg-max (R13); a span is split
 only when its centre commits (R14); credit changes only on masked rows (R16);
-``out_tokens`` holds the candidate of every row (R17).
+``out_tokens`` holds the candidate of every row (R17); the optional top-k export ranks
+float32-rounded logits with ties to the lower id and gives full-vocabulary probabilities (T1-T4).
 
 Precision.  Logits and the softmax sum are float64 over the exact input
 values (bfloat16 products are exact).  Where a float decides an integer the
@@ -131,6 +132,46 @@ def token_stats(hidden: np.ndarray, W: np.ndarray, row_chunk: int = 64) -> dict:
         tok[r0:r0 + z.shape[0]] = t
     shape = hidden.shape[:-1]
     return {"conf": conf.reshape(shape), "tok": tok.reshape(shape), "gap": gap.reshape(shape)}
+
+
+def topk_candidates(hidden: np.ndarray, W: np.ndarray, k: int, row_chunk: int = 64) -> dict:
+    """The ``k`` best candidates of every row and their softmax probabilities.
+
+    The explainer's iteration-manager paragraph says the information of the candidates a step
+    does not choose is carried into the next iteration, without saying in what form.  This is
+    the data such a scheme starts from (readings T1-T4):
+
+    * ``tok[r, i]``: the token with the i-th largest float32-rounded logit, ties to the lower
+      id (the arg-max rule R2 extended), so ``tok[:, 0]`` is the candidate of
+      :func:`token_stats`;
+    * ``prob[r, i]`` = ``exp(z_tok - max z) / sum_v exp(z_v - max z)`` in float64, returned
+      as float32: its softmax probability, so ``prob[:, 0]`` is the confidence;
+    * when ``k > V`` the entries past ``V`` are token -1 with probability 0;
+    * every row is ranked, masked or not (like the candidate of R17).
+    """
+    if k < 1:
+        raise ValueError("k must be >= 1")
+    hidden = np.asarray(hidden)
+    H = W.shape[1]
+    V = W.shape[0]
+    h2 = hidden.reshape(-1, H)
+    M = h2.shape[0]
+    tok = np.full((M, k), -1, dtype=np.int64)
+    prob = np.zeros((M, k), dtype=np.float32)
+    kk = min(k, V)
+    for r0 in range(0, M, row_chunk):
+        z = lm_head_logits(h2[r0:r0 + row_chunk], W)
+        z32 = z.astype(np.float32)
+        # a stable sort of the negated logits keeps equal logits in ascending id order
+        order = np.argsort(-z32, axis=1, kind="stable")[:, :kk]
+        zmax = z.max(axis=1, keepdims=True)
+        e = np.exp(z - zmax)
+        S = e.sum(axis=1, keepdims=True)
+        rows = np.arange(z.shape[0])[:, None]
+        tok[r0:r0 + z.shape[0], :kk] = order
+        prob[r0:r0 + z.shape[0], :kk] = (e[rows, order] / S).astype(np.float32)
+    shape = hidden.shape[:-1] + (k,)
+    return {"tok": tok.reshape(shape), "prob": prob.reshape(shape)}
 
 
 # --------------------------------------------------------------------------------------------
