@@ -21,7 +21,7 @@ DLM_F32, DLM_BF16 = 0, 1
 DLM_THRESHOLD, DLM_HIERARCHICAL, DLM_CREDIT = 0, 1, 2
 DLM_AUTO_ADVANCE = 1
 DLM_SEQ_RUNNING, DLM_SEQ_FINISHED, DLM_SEQ_EOS_IN_BLOCK = 0, 1, 2
-DLM_MAX_SEQS, DLM_MAX_L, DLM_CREDIT_SLOTS, DLM_MAX_RULES = 256, 64, 4, 8
+DLM_MAX_SEQS, DLM_MAX_L, DLM_CREDIT_SLOTS, DLM_MAX_RULES, DLM_MAX_TOPK = 256, 64, 4, 8, 8
 
 STATUS_NAMES = {0: "DLM_OK", -1: "DLM_ERR_NULL", -2: "DLM_ERR_DTYPE", -3: "DLM_ERR_SHAPE",
                 -4: "DLM_ERR_POLICY", -5: "DLM_ERR_WORKSPACE", -6: "DLM_ERR_HIP"}
@@ -43,7 +43,8 @@ class dlm_policy(ctypes.Structure):
                 ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
                 ("stream", ctypes.c_void_p),
                 ("out_conf", ctypes.c_void_p), ("out_gap", ctypes.c_void_p),
-                ("seq_done", ctypes.c_void_p)]
+                ("seq_done", ctypes.c_void_p),
+                ("topk", ctypes.c_int32), ("out_topk_tokens", ctypes.c_void_p), ("out_topk_prob", ctypes.c_void_p)]
 
 
 class DlmError(RuntimeError):
@@ -75,6 +76,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dlm_commit.restype = ctypes.c_int
     lib.dlm_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     lib.dlm_workspace_bytes.restype = ctypes.c_size_t
+    lib.dlm_workspace_bytes_topk.argtypes = [i64, i64, i64, i64, i32, i32]
+    lib.dlm_workspace_bytes_topk.restype = ctypes.c_size_t
     lib.dlm_workspace_init.argtypes = [vp, ctypes.c_size_t, vp]
     lib.dlm_workspace_init.restype = ctypes.c_int
     lib.dlm_last_error.argtypes = []
@@ -116,7 +119,7 @@ class StepPolicy:
 
     def __init__(self, B: int, L: int, H: int, V: int, dtype: int, seq: Sequence, workspace=None,
                  workspace_bytes: Optional[int] = None, flags: int = 0, stream=None, out_conf=None, out_gap=None,
-                 seq_done=None):
+                 seq_done=None, topk: int = 0, out_topk_tokens=None, out_topk_prob=None):
         self._seq = (dlm_seq_policy * max(1, len(seq)))()
         for i, s in enumerate(seq):
             if hasattr(s, "kind"):
@@ -134,6 +137,7 @@ class StepPolicy:
         self.c.out_conf = _ptr(out_conf)
         self.c.out_gap = _ptr(out_gap)
         self.c.seq_done = _ptr(seq_done)
+        self.set_topk(topk, out_topk_tokens, out_topk_prob)
         self._keep = (workspace, out_conf, out_gap, seq_done)
 
     def set_workspace(self, workspace, nbytes: Optional[int] = None) -> None:
@@ -147,6 +151,12 @@ class StepPolicy:
 
     def set_seq_done(self, seq_done=None) -> None:
         self.c.seq_done = _ptr(seq_done)
+
+    def set_topk(self, topk: int = 0, out_topk_tokens=None, out_topk_prob=None) -> None:
+        self.c.topk = int(topk)
+        self.c.out_topk_tokens = _ptr(out_topk_tokens)
+        self.c.out_topk_prob = _ptr(out_topk_prob)
+        self._keep_topk = (out_topk_tokens, out_topk_prob)
 
     def set_outputs(self, out_conf=None, out_gap=None) -> None:
         self.c.out_conf = _ptr(out_conf)
@@ -177,6 +187,10 @@ def dlm_commit(conf, tokens, mask_state, credit_state, policy: StepPolicy, out_c
 
 def dlm_workspace_bytes(B: int, L: int, H: int, V: int, dtype: int) -> int:
     return int(load().dlm_workspace_bytes(B, L, H, V, dtype))
+
+
+def dlm_workspace_bytes_topk(B: int, L: int, H: int, V: int, dtype: int, topk: int) -> int:
+    return int(load().dlm_workspace_bytes_topk(B, L, H, V, dtype, topk))
 
 
 def dlm_workspace_init(workspace, workspace_bytes: Optional[int] = None, stream=None) -> None:

@@ -12,7 +12,7 @@
 #include "dlm.h"
 #include "dlm_device.hpp"
 
-static_assert(sizeof(dlm_seq_policy) == 20 && sizeof(dlm_policy) == 96 && sizeof(dlm_credit_slot) == 8,
+static_assert(sizeof(dlm_seq_policy) == 20 && sizeof(dlm_policy) == 120 && sizeof(dlm_credit_slot) == 8,
               "C ABI struct layout (the Python binding mirrors it)");
 
 namespace {
@@ -48,11 +48,15 @@ struct Plan {
   size_t lds = 0;    // dynamic LDS bytes
   size_t ws = 0;     // workspace bytes
   size_t packed_off = 0, packed_bytes = 0;  // GEMM path: fragment-ordered hidden rows in the workspace
+  int topk = 0;      // streaming kernel with the top-k fold + finalize_topk_kernel
+  size_t topk_off = 0;                      // top-k records in the workspace
 };
 
 int elem_bytes(int32_t dtype) { return dtype == DLM_BF16 ? 2 : dtype == DLM_F32 ? 4 : 0; }
 
-int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p) {
+// topk > 0 selects the streaming kernel with the top-k fold for every shape (the GEMM-shaped head
+// has none) and appends its records to the workspace; the caller validates topk's range.
+int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int topk, Plan* p) {
   const int es = elem_bytes(dtype);
   if (!es) return fail(DLM_ERR_DTYPE, "dtype %d is neither DLM_F32 (0) nor DLM_BF16 (1)", (int)dtype);
   if (B < 1 || B > DLM_MAX_SEQS) return fail(DLM_ERR_SHAPE, "B=%lld outside [1, %d]", (long long)B, DLM_MAX_SEQS);
@@ -63,7 +67,7 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
   const int64_t ntiles = (V + dlm::kTileRows - 1) / dlm::kTileRows;
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
   const int64_t m_pad = (M + 31) / 32 * 32;
-  if (dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && m_pad * H * 2 < (1ll << 31)) {
+  if (!topk && dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && m_pad * H * 2 < (1ll << 31)) {
     // GEMM-shaped path: 256-row vocabulary tiles against 256-row groups; workgroups per row group
     // a multiple of 8 where possible (so the groups of one tile can share an XCD)
     const int64_t BN = dlm::GemmWide::BN;
@@ -115,6 +119,14 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, Plan* p
   p->ntiles = (int)ntiles;
   p->lds = dlm::lds_bytes(NMB);
   p->ws = kTicketBytes + (size_t)n_rg * MR * G_v * 16;
+  if (topk) {
+    // ticket | records [n_rg * MR][G_v] | top-k records [n_rg * MR][G_v] x DLM_MAX_TOPK x 8 bytes
+    if (n_rg * MR * G_v * (DLM_MAX_TOPK * 8) >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large for top-k");
+    p->topk = 1;
+    p->topk_off = p->ws;
+    p->ws += (size_t)n_rg * MR * G_v * (DLM_MAX_TOPK * 8);
+    p->lds = dlm::lds_bytes_topk(NMB);
+  }
   return DLM_OK;
 }
 
@@ -162,32 +174,44 @@ int pack_rules(const dlm_policy* pol, bool need_credit_state, const void* credit
   return DLM_OK;
 }
 
-template <class T, int NMB, int KFWM>
+template <class T, int NMB, int KFWM, bool TK>
 int launch_step(const dlm::StepArgs& a, const Plan& p, hipStream_t stream) {
-  hipLaunchKernelGGL((dlm::step_kernel<T, NMB, KFWM>), dim3(p.n_rg * p.G_v), dim3(dlm::kThreads), p.lds, stream, a);
+  hipLaunchKernelGGL((dlm::step_kernel<T, NMB, KFWM, TK>), dim3(p.n_rg * p.G_v), dim3(dlm::kThreads), p.lds, stream,
+                     a);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DLM_ERR_HIP, "step kernel launch: %s", hipGetErrorString(e));
   return ok();
 }
 
-template <class T>
+template <class T, bool TK>
 int launch_step_for(const dlm::StepArgs& a, const Plan& p, hipStream_t stream) {
   switch (p.NMB * 100 + p.KFWM) {
-    case 102: return launch_step<T, 1, 2>(a, p, stream);
-    case 108: return launch_step<T, 1, 8>(a, p, stream);
-    case 116: return launch_step<T, 1, 16>(a, p, stream);
-    case 202: return launch_step<T, 2, 2>(a, p, stream);
-    case 208: return launch_step<T, 2, 8>(a, p, stream);
-    case 216: return launch_step<T, 2, 16>(a, p, stream);
-    case 402: return launch_step<T, 4, 2>(a, p, stream);
-    case 408: return launch_step<T, 4, 8>(a, p, stream);
+    case 102: return launch_step<T, 1, 2, TK>(a, p, stream);
+    case 108: return launch_step<T, 1, 8, TK>(a, p, stream);
+    case 116: return launch_step<T, 1, 16, TK>(a, p, stream);
+    case 202: return launch_step<T, 2, 2, TK>(a, p, stream);
+    case 208: return launch_step<T, 2, 8, TK>(a, p, stream);
+    case 216: return launch_step<T, 2, 16, TK>(a, p, stream);
+    case 402: return launch_step<T, 4, 2, TK>(a, p, stream);
+    case 408: return launch_step<T, 4, 8, TK>(a, p, stream);
     default: return fail(DLM_ERR_SHAPE, "no kernel for NMB=%d KFWM=%d", p.NMB, p.KFWM);
   }
 }
 
+// Top-k fields of the policy: range and output pointer (before any launch).
+int check_topk(const dlm_policy* pol, dlm::CommitArgs* c) {
+  if (pol->topk < 0 || pol->topk > DLM_MAX_TOPK)
+    return fail(DLM_ERR_POLICY, "topk=%d outside [0, %d]", (int)pol->topk, DLM_MAX_TOPK);
+  if (pol->topk > 0 && !pol->out_topk_tokens) return fail(DLM_ERR_NULL, "topk > 0 but out_topk_tokens is NULL");
+  c->topk = pol->topk;
+  c->out_topk_tokens = pol->topk > 0 ? pol->out_topk_tokens : nullptr;
+  c->out_topk_prob = pol->topk > 0 ? pol->out_topk_prob : nullptr;
+  return DLM_OK;
+}
+
 int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::CommitArgs c, bool commit) {
   Plan p;
-  int rc = make_plan(pol->B, pol->L, pol->H, pol->V, pol->dtype, &p);
+  int rc = make_plan(pol->B, pol->L, pol->H, pol->V, pol->dtype, c.topk, &p);
   if (rc) return rc;
   if (!pol->workspace) return fail(DLM_ERR_NULL, "policy->workspace is NULL");
   if (pol->workspace_bytes < p.ws)
@@ -205,6 +229,7 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   a.n_rg = p.n_rg;
   a.G_v = p.G_v;
   a.ntiles = p.ntiles;
+  a.topk_records = p.topk ? reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.topk_off) : nullptr;
   c.B = (int)pol->B;
   c.L = (int)pol->L;
   c.flags = (commit ? dlm::kFlagCommit : 0u) | (commit ? (pol->flags & DLM_AUTO_ADVANCE) : 0u);
@@ -241,7 +266,19 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "finalize kernel launch: %s", hipGetErrorString(e));
     return ok();
   }
-  return pol->dtype == DLM_BF16 ? launch_step_for<uint16_t>(a, p, stream) : launch_step_for<float>(a, p, stream);
+  if (p.topk) {
+    rc = pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, true>(a, p, stream) : launch_step_for<float, true>(a, p, stream);
+    if (rc) return rc;
+    const int rows = 16 * p.NMB;
+    const int M = a.M;
+    const int grid = c.B + (M + dlm::kWaves - 1) / dlm::kWaves;
+    hipLaunchKernelGGL(dlm::finalize_topk_kernel, dim3(grid), dim3(dlm::kThreads), 0, stream, a.c, a.partials,
+                       a.topk_records, p.G_v, p.n_rg * rows);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(DLM_ERR_HIP, "top-k finalize kernel launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  return pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, false>(a, p, stream) : launch_step_for<float, false>(a, p, stream);
 }
 
 }  // namespace
@@ -255,8 +292,10 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
     return fail(DLM_ERR_NULL, "hidden, W_vocab, mask_state, out_tokens and out_commit must be non-NULL");
   dlm::CommitArgs c;
   std::memset(&c, 0, sizeof c);
+  int rc = check_topk(policy, &c);
+  if (rc) return rc;
   Plan p;
-  int rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, &p);
+  rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, c.topk, &p);
   if (rc) return rc;
   rc = pack_rules(policy, true, credit_state, policy->V, &c);
   if (rc) return rc;
@@ -278,8 +317,10 @@ int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mas
   if (n_steps < 1) return fail(DLM_ERR_SHAPE, "n_steps=%lld must be >= 1", (long long)n_steps);
   dlm::CommitArgs c;
   std::memset(&c, 0, sizeof c);
+  int rc = check_topk(policy, &c);
+  if (rc) return rc;
   Plan p;
-  int rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, &p);
+  rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, c.topk, &p);
   if (rc) return rc;
   rc = pack_rules(policy, true, credit_state, policy->V, &c);
   if (rc) return rc;
@@ -291,9 +332,15 @@ int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mas
   c.credit = credit_state;
   c.out_conf = policy->out_conf;
   c.out_gap = policy->out_gap;
+  int32_t* const topk_tokens0 = c.out_topk_tokens;
+  float* const topk_prob0 = c.out_topk_prob;
   for (int64_t n = 0; n < n_steps; ++n) {
     c.out_tokens = out_tokens_steps + n * rows;
     c.out_commit = out_commit_steps + n * rows;
+    if (c.topk) {
+      c.out_topk_tokens = topk_tokens0 + (size_t)n * rows * c.topk;
+      c.out_topk_prob = topk_prob0 ? topk_prob0 + (size_t)n * rows * c.topk : nullptr;
+    }
     rc = run_step(static_cast<const char*>(hidden_steps) + n * step_bytes, W_vocab, policy, c, true);
     if (rc) return rc;  // only a failed launch can get here, after validation passed
   }
@@ -307,6 +354,8 @@ int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* p
     return fail(DLM_ERR_NULL, "hidden, W_vocab, out_conf and out_tokens must be non-NULL");
   dlm::CommitArgs c;
   std::memset(&c, 0, sizeof c);
+  const int rc = check_topk(policy, &c);
+  if (rc) return rc;
   c.out_tokens = out_tokens;
   c.out_conf = out_conf;
   c.out_gap = out_gap;
@@ -342,9 +391,14 @@ int dlm_commit(const float* conf, const int32_t* tokens, uint8_t* mask_state, dl
 }
 
 size_t dlm_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype) {
+  return dlm_workspace_bytes_topk(B, L, H, V, dtype, 0);
+}
+
+size_t dlm_workspace_bytes_topk(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int32_t topk) {
+  if (topk < 0 || topk > DLM_MAX_TOPK) return 0;
   Plan p;
   const std::string saved = g_last_error;
-  const int rc = make_plan(B, L, H, V, dtype, &p);
+  const int rc = make_plan(B, L, H, V, dtype, topk, &p);
   g_last_error = saved;
   return rc ? 0 : p.ws;
 }

@@ -48,6 +48,9 @@ struct CommitArgs {
   float* out_conf;
   float* out_gap;
   uint8_t* seq_done;   // [B] early-stop state (DLM_SEQ_*), or null
+  int32_t* out_topk_tokens;  // [B*L][topk] top-k export, or null (topk == 0)
+  float* out_topk_prob;      // [B*L][topk] or null
+  int topk;
   int B, L;
   unsigned flags;
   Rule rules[DLM_MAX_RULES];
@@ -61,6 +64,13 @@ __host__ __device__ constexpr size_t lds_bytes(int NMB) {
                                                                       : (size_t)kRowsPerStage * 8;
 }
 
+// With the top-k fold the per-slot statistics (16 bytes) are followed by the per-slot lists
+// (DLM_MAX_TOPK entries of 8 bytes) of the 256 * NMB logit slots of a tile.
+__host__ __device__ constexpr size_t lds_bytes_topk(int NMB) {
+  return lds_bytes(NMB) > (size_t)256 * NMB * (16 + DLM_MAX_TOPK * 8) ? lds_bytes(NMB)
+                                                                        : (size_t)256 * NMB * (16 + DLM_MAX_TOPK * 8);
+}
+
 struct StepArgs {
   const void* hidden;  // [M][H]
   const void* W;       // [V][H]
@@ -70,6 +80,7 @@ struct StepArgs {
   int n_rg;            // row groups of 16 * NMB rows
   int G_v;             // vocabulary ranges (multiple of 8)
   int ntiles;          // ceil(V / 16)
+  float4* topk_records;  // top-k fold only: [n_rg * 16 * NMB][G_v] lists of kTopK (logit, id)
   CommitArgs c;
 };
 
@@ -178,6 +189,77 @@ __device__ __forceinline__ Stats stats_row16_merge(Stats t) {
   t = stats_merge(t, stats_dpp<kDppHalfMirror>(t));
   t = stats_merge(t, stats_dpp<kDppMirror>(t));
   return t;
+}
+
+// ----------------------------------------------------------------------------------------------
+// Top-k candidates: a best-first list of (logit, token id).  Larger logits first; among equal
+// logits the lower id first.  An empty entry is (-inf, kNoToken).
+// ----------------------------------------------------------------------------------------------
+constexpr int kTopK = DLM_MAX_TOPK;
+constexpr int kNoToken = 0x7fffffff;
+
+struct TopK {
+  float z[kTopK];
+  int id[kTopK];
+};
+
+__device__ __forceinline__ void topk_clear(TopK& t) {
+#pragma unroll
+  for (int i = 0; i < kTopK; ++i) {
+    t.z[i] = -INFINITY;
+    t.id[i] = kNoToken;
+  }
+}
+
+// Insert logit z of token v, where v is larger than every id already in the list (a thread meets
+// its tokens in ascending order), so v goes behind equal logits.  Branch-free: from the bottom
+// up, entry i takes entry i - 1, the new value, or keeps its own.
+__device__ __forceinline__ void topk_push_ascending(TopK& t, float z, int v) {
+#pragma unroll
+  for (int i = kTopK - 1; i > 0; --i) {
+    const bool up = z > t.z[i - 1];
+    const bool here = z > t.z[i];
+    t.id[i] = up ? t.id[i - 1] : here ? v : t.id[i];
+    t.z[i] = up ? t.z[i - 1] : here ? z : t.z[i];
+  }
+  if (z > t.z[0]) {
+    t.id[0] = v;
+    t.z[0] = z;
+  }
+}
+
+// Drop the head of the list where `pop` holds (an empty entry enters at the bottom).
+__device__ __forceinline__ void topk_pop_if(TopK& t, bool pop) {
+#pragma unroll
+  for (int i = 0; i < kTopK - 1; ++i) {
+    t.z[i] = pop ? t.z[i + 1] : t.z[i];
+    t.id[i] = pop ? t.id[i + 1] : t.id[i];
+  }
+  t.z[kTopK - 1] = pop ? -INFINITY : t.z[kTopK - 1];
+  t.id[kTopK - 1] = pop ? kNoToken : t.id[kTopK - 1];
+}
+
+// Every lane of a 16-lane row ends with the kTopK best entries of the row's 16 lists: each round
+// takes the best head (largest logit, then lowest id) and pops it from the list that held it.
+// Token ids are distinct across the lists, so exactly one list pops (or only empty heads).
+__device__ __forceinline__ void topk_row16_merge(TopK& t, TopK& out) {
+#pragma unroll
+  for (int r = 0; r < kTopK; ++r) {
+    const float hz = t.z[0];
+    const int hi = t.id[0];
+    float m = fmaxf(hz, dpp<kDppXor1>(hz));
+    m = fmaxf(m, dpp<kDppXor2>(m));
+    m = fmaxf(m, dpp<kDppHalfMirror>(m));
+    m = fmaxf(m, dpp<kDppMirror>(m));
+    int id = hz == m ? hi : kNoToken;
+    id = min(id, dpp<kDppXor1>(id));
+    id = min(id, dpp<kDppXor2>(id));
+    id = min(id, dpp<kDppHalfMirror>(id));
+    id = min(id, dpp<kDppMirror>(id));
+    out.z[r] = m;
+    out.id[r] = id;
+    topk_pop_if(t, hz == m && hi == id);
+  }
 }
 
 // Statistics records are exchanged between workgroups with 16-byte buffer accesses carrying the
@@ -561,8 +643,12 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
 // the device coherence point; the last workgroup to finish (completion counter) merges the
 // records of every row in a fixed order, derives conf / token / gap and runs each sequence's
 // commit policy on one wavefront.
+//
+// With TK (top-k export) every thread also keeps the DLM_MAX_TOPK best logits of its slot, the
+// workgroup merges them per row into a second record, and the kernel ends there:
+// finalize_topk_kernel merges, commits and writes the export.
 // ----------------------------------------------------------------------------------------------
-template <class T, int NMB, int KFWM>
+template <class T, int NMB, int KFWM, bool TK>
 __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   extern __shared__ uint4 smem[];
   using E = Elem<T>;
@@ -638,8 +724,12 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   // ---- stream the tiles -------------------------------------------------------------------------
   float* red = reinterpret_cast<float*>(smem);           // [2][kWaves][NMB][64 lanes][4] partials
   Stats st[P];
+  TopK tk[TK ? P : 1];
 #pragma unroll
-  for (int p = 0; p < P; ++p) st[p] = stats_empty();
+  for (int p = 0; p < P; ++p) {
+    st[p] = stats_empty();
+    if constexpr (TK) topk_clear(tk[p]);
+  }
   f32x4 acc[NMB];
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -673,7 +763,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
 #pragma unroll
             for (int w = 0; w < kWaves; ++w) z += buf[(w * NMB + mb) * 256 + rest];
             const int v = (t_begin + r) * kTileRows + 4 * (rest >> 6) + (rest & 3);
-            if (v < a.V) stats_fold1(st[p], z, v);
+            if (v < a.V) {
+              stats_fold1(st[p], z, v);
+              if constexpr (TK) topk_push_ascending(tk[p], z, v);
+            }
           }
         }
       }
@@ -683,10 +776,17 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   // ---- merge each row's 16 slots inside the workgroup; one record per row -----------------------
   __syncthreads();
   float4* slots = reinterpret_cast<float4*>(smem);       // [LOGITS] statistics, by slot
+  float2* lists = reinterpret_cast<float2*>(slots + LOGITS);   // [kTopK][LOGITS] (logit, id)
 #pragma unroll
   for (int p = 0; p < P; ++p) {
     const int f = tid + p * kThreads;
-    if (f < LOGITS) slots[f] = stats_pack(st[p]);
+    if (f < LOGITS) {
+      slots[f] = stats_pack(st[p]);
+      if constexpr (TK) {
+#pragma unroll
+        for (int i = 0; i < kTopK; ++i) lists[i * LOGITS + f] = make_float2(tk[p].z[i], __int_as_float(tk[p].id[i]));
+      }
+    }
   }
   __syncthreads();
   const __amdgpu_buffer_rsrc_t rec = __builtin_amdgcn_make_buffer_rsrc(
@@ -697,11 +797,32 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
     const int f = (rr >> 4) * 256 + 64 * (k >> 2) + 4 * (rr & 15) + (k & 3);
     const Stats t = stats_row16_merge(stats_unpack(slots[f]));
     if (k == 0) record_store(rec, (unsigned)((((size_t)rg * MR + rr) * a.G_v + gv) * 16), stats_pack(t));
+    if constexpr (TK) {
+      TopK mine, best;
+#pragma unroll
+      for (int i = 0; i < kTopK; ++i) {
+        const float2 e = lists[i * LOGITS + f];
+        mine.z[i] = e.x;
+        mine.id[i] = __float_as_int(e.y);
+      }
+      topk_row16_merge(mine, best);
+      if (k == 0) {
+        const __amdgpu_buffer_rsrc_t trec = __builtin_amdgcn_make_buffer_rsrc(
+            a.topk_records, 0, a.n_rg * MR * a.G_v * (kTopK * 8), 0x00020000);
+        const unsigned off = (unsigned)((((size_t)rg * MR + rr) * a.G_v + gv) * (kTopK * 8));
+#pragma unroll
+        for (int j = 0; j < kTopK / 2; ++j)
+          record_store(trec, off + 16u * j,
+                       make_float4(best.z[2 * j], __int_as_float(best.id[2 * j]), best.z[2 * j + 1],
+                                   __int_as_float(best.id[2 * j + 1])));
+      }
+    }
   }
   // The records must be complete before this workgroup is counted; device-scope stores need no
   // cache write-back, only the wait for their acknowledgement.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if constexpr (TK) return;   // finalize_topk_kernel follows on the stream
 
   // ---- the last workgroup merges every row and commits ------------------------------------------
   // Wrapping increment: the counter runs 0 .. gridDim.x-1 and the last arrival puts it back to 0,
@@ -1091,6 +1212,88 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, 
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   if (do_commit && wave == 0) pre = load_seq_state(c, b);
   finalize_sequences(c, rec, G, b, b + 1, stage, pre, wave == 0 ? b : -1);
+}
+
+// Top-k export of one row (one wavefront): the G best-first lists of the row (lists g = lane,
+// lane + 64, ... per lane) are merged by taking the best head kTopK times, lowest id among equal
+// logits.  A candidate's probability is 2^((z - M) log2 e) / S with the row's maximum M and sum S,
+// so entry 0 equals the row's confidence.
+__device__ __forceinline__ void topk_finalize_row(const CommitArgs& c, __amdgpu_buffer_rsrc_t trec, int G, int row,
+                                                  float M, float inv_s) {
+  constexpr int N = kMaxVocabGroups / 64;
+  const int lane = __lane_id();
+  TopK t[N];
+  const unsigned base = (unsigned)row * (unsigned)G * (kTopK * 8u);
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int g = lane + 64 * n;
+    topk_clear(t[n]);
+    if (g < G) {
+#pragma unroll
+      for (int j = 0; j < kTopK / 2; ++j) {
+        const float4 e = record_load(trec, base + (unsigned)g * (kTopK * 8u) + 16u * j);
+        t[n].z[2 * j] = e.x;
+        t[n].id[2 * j] = __float_as_int(e.y);
+        t[n].z[2 * j + 1] = e.z;
+        t[n].id[2 * j + 1] = __float_as_int(e.w);
+      }
+    }
+  }
+  const size_t out0 = (size_t)row * c.topk;
+  for (int r = 0; r < c.topk; ++r) {
+    float bz = t[0].z[0];
+    int bi = t[0].id[0], bn = 0;
+#pragma unroll
+    for (int n = 1; n < N; ++n) {
+      const bool better = t[n].z[0] > bz || (t[n].z[0] == bz && t[n].id[0] < bi);
+      bz = better ? t[n].z[0] : bz;
+      bi = better ? t[n].id[0] : bi;
+      bn = better ? n : bn;
+    }
+    const float m = wave_max(bz);
+    const int id = wave_allreduce_min(bz == m ? bi : kNoToken);
+    const bool win = bz == m && bi == id;
+#pragma unroll
+    for (int n = 0; n < N; ++n) topk_pop_if(t[n], win && bn == n);
+    if (lane == 0) {
+      const bool real = id != kNoToken;
+      c.out_topk_tokens[out0 + r] = real ? id : -1;
+      if (c.out_topk_prob) c.out_topk_prob[out0 + r] = real ? fminf(ex2((m - M) * kLog2e) * inv_s, 1.f) : 0.f;
+    }
+  }
+}
+
+// Merge + commit after the streaming kernel with the top-k fold.  Workgroups [0, B) merge and
+// commit one sequence each, as finalize_kernel; the others take one row per wavefront: they merge
+// its statistics records again (same order, same result) for M and S, then its top-k records.
+__global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArgs c, const float4* records,
+                                                                 const float4* topk_records, int G,
+                                                                 int nrows_total) {
+  __shared__ uint4 stage[kRowsPerStage / 2];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rec =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
+  if ((int)blockIdx.x < c.B) {
+    const int b = blockIdx.x;
+    SeqState pre;
+    const bool do_commit = (c.flags & kFlagCommit) != 0;
+    if (do_commit && wave == 0) pre = load_seq_state(c, b);
+    finalize_sequences(c, rec, G, b, b + 1, stage, pre, wave == 0 ? b : -1);
+    return;
+  }
+  const int row = ((int)blockIdx.x - c.B) * kWaves + wave;
+  if (row >= c.B * c.L) return;
+  const int lane = threadIdx.x & 63;
+  float4 r[kMaxVocabGroups / 64];
+#pragma unroll
+  for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
+    const int g = lane + 64 * i;
+    r[i] = g < G ? record_load(rec, (unsigned)(((size_t)row * G + g) * 16)) : stats_pack(stats_empty());
+  }
+  const Stats t = merge_records(r);
+  const __amdgpu_buffer_rsrc_t trec = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float4*>(topk_records), 0, nrows_total * G * (kTopK * 8), 0x00020000);
+  topk_finalize_row(c, trec, G, row, t.m1, 1.f / t.s);
 }
 
 // dlm_commit: conf / tokens given, one wavefront per sequence.

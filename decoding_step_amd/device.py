@@ -47,12 +47,13 @@ def credit_from_numpy(tok: np.ndarray, val: np.ndarray, device="cuda") -> torch.
 class Decoder:
     """One decode step on device buffers it owns: workspace, outputs and diagnostics."""
 
-    def __init__(self, W: torch.Tensor, B: int, L: int, seq, flags: int = 0, stream=None, diagnostics: bool = True):
+    def __init__(self, W: torch.Tensor, B: int, L: int, seq, flags: int = 0, stream=None, diagnostics: bool = True,
+                 topk: int = 0):
         V, H = W.shape
         self.W, self.B, self.L, self.H, self.V = W, B, L, H, V
         dev = W.device
         code = torch_dtype_code(W)
-        nbytes = nat.dlm_workspace_bytes(B, L, H, V, code)
+        nbytes = nat.dlm_workspace_bytes_topk(B, L, H, V, code, topk)
         if nbytes == 0:
             raise nat.DlmError(nat.DLM_ERR_SHAPE, f"unsupported shapes B={B} L={L} H={H} V={V}")
         self.workspace = torch.zeros(nbytes, dtype=torch.uint8, device=dev)
@@ -60,17 +61,28 @@ class Decoder:
         self.out_commit = torch.empty((B, L), dtype=torch.uint8, device=dev)
         self.conf = torch.empty((B, L), dtype=torch.float32, device=dev) if diagnostics else None
         self.gap = torch.empty((B, L), dtype=torch.float32, device=dev) if diagnostics else None
+        self.topk = topk
+        self.topk_tokens = torch.empty((B, L, topk), dtype=torch.int32, device=dev) if topk else None
+        self.topk_prob = torch.empty((B, L, topk), dtype=torch.float32, device=dev) if topk else None
         self.policy = nat.StepPolicy(B, L, H, V, code, seq, self.workspace, flags=flags, stream=stream,
-                                     out_conf=self.conf, out_gap=self.gap)
+                                     out_conf=self.conf, out_gap=self.gap, topk=topk,
+                                     out_topk_tokens=self.topk_tokens, out_topk_prob=self.topk_prob)
 
     def step(self, hidden: torch.Tensor, mask: torch.Tensor, credit=None) -> None:
         nat.dlm_decode_step(hidden, self.W, mask, credit, self.policy, self.out_tokens, self.out_commit)
 
     def steps(self, hidden_steps: torch.Tensor, mask: torch.Tensor, credit, out_tokens: torch.Tensor,
-              out_commit: torch.Tensor) -> None:
-        """hidden_steps[n] for step n; per-step outputs [n][B][L] (dlm_decode_steps)."""
-        nat.dlm_decode_steps(hidden_steps, self.W, mask, credit, self.policy, hidden_steps.shape[0], out_tokens,
-                             out_commit)
+              out_commit: torch.Tensor, out_topk_tokens=None, out_topk_prob=None) -> None:
+        """hidden_steps[n] for step n; per-step outputs [n][B][L] (dlm_decode_steps), and with top-k on
+        per-step exports [n][B][L][topk] (the Decoder's own single-step buffers when not given)."""
+        if self.topk and out_topk_tokens is not None:
+            self.policy.set_topk(self.topk, out_topk_tokens, out_topk_prob)
+        try:
+            nat.dlm_decode_steps(hidden_steps, self.W, mask, credit, self.policy, hidden_steps.shape[0], out_tokens,
+                                 out_commit)
+        finally:
+            if self.topk:
+                self.policy.set_topk(self.topk, self.topk_tokens, self.topk_prob)
 
     def token_stats(self, hidden: torch.Tensor, conf: torch.Tensor, tokens: torch.Tensor, gap=None) -> None:
         nat.dlm_token_stats(hidden, self.W, self.policy, conf, tokens, gap)

@@ -38,12 +38,13 @@
 extern "C" {
 #endif
 
-#define DLM_VERSION_STRING "0.2.0"
+#define DLM_VERSION_STRING "0.3.0"
 
 #define DLM_MAX_SEQS 256   /* sequences per call                                  */
 #define DLM_MAX_L 64       /* positions per block: one wavefront lane per position */
 #define DLM_CREDIT_SLOTS 4 /* tracked (token, credit) candidates per position      */
 #define DLM_MAX_RULES 8    /* distinct dlm_seq_policy values per call              */
+#define DLM_MAX_TOPK 8     /* candidates per row in the top-k export               */
 
 /* Status codes. */
 enum {
@@ -118,7 +119,27 @@ typedef struct {
   float* out_gap;            /* optional device [B][L]: top-1 minus top-2 logit, or NULL   */
   uint8_t* seq_done;         /* optional device [B], in/out: early-stop state (DLM_SEQ_*);
                                 NULL disables early stop for every sequence                 */
+  int32_t topk;              /* top-k export: 0 = off, 1..DLM_MAX_TOPK candidates per row   */
+  int32_t* out_topk_tokens;  /* device [B][L][topk] int32 when topk > 0 (see below)         */
+  float* out_topk_prob;      /* optional device [B][L][topk] float, or NULL                 */
 } dlm_policy;
+
+/*
+ * Top-k candidate export (policy->topk > 0; dlm_decode_step, dlm_decode_steps and
+ * dlm_token_stats).  The explainer's diffusion-iteration manager carries the information of the
+ * candidates a step does not choose into the next iteration; the step exports that raw material
+ * from the same pass over W_vocab.  For EVERY row (masked or not):
+ *   out_topk_tokens[r][i]  the token with the i-th largest logit (float32), ties to the lower
+ *                          id, so entry 0 is the candidate in out_tokens;
+ *   out_topk_prob[r][i]    its softmax probability over the whole vocabulary,
+ *                          exp(z - max z) / sum_v exp(z_v - max z), so entry 0 is the confidence;
+ *   entries past V         token -1, probability 0.
+ * The workspace must hold dlm_workspace_bytes_topk(B, L, H, V, dtype, topk) bytes.  With top-k
+ * on, every shape takes the streaming LM head (the GEMM-shaped head for B*L > 64 has no top-k
+ * fold), followed by a separate merge kernel.  Errors: topk outside 0..DLM_MAX_TOPK gives
+ * DLM_ERR_POLICY, topk > 0 with out_topk_tokens NULL gives DLM_ERR_NULL, a workspace smaller
+ * than the top-k size gives DLM_ERR_WORKSPACE.
+ */
 
 /*
  * One decode step.
@@ -152,7 +173,8 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
  *   out_tokens_steps  [n_steps][B][L]     int32
  *   out_commit_steps  [n_steps][B][L]     uint8
  *   n_steps           >= 1 (DLM_ERR_SHAPE otherwise)
- * policy->out_conf / out_gap, if set, hold the last step's values.  Everything is validated
+ * policy->out_conf / out_gap, if set, hold the last step's values; with policy->topk > 0,
+ * out_topk_tokens / out_topk_prob are [n_steps][B][L][topk], step n at offset n*B*L*topk.  Everything is validated
  * before the first launch; on error nothing is enqueued.  The call allocates nothing, waits for
  * nothing and records no memset, so it may be captured into a HIP graph and replayed.
  */
@@ -162,8 +184,9 @@ int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mas
 
 /*
  * LM head + per-row statistics only (no commit): for every row, the
- * confidence, the candidate token and the top-2 logit gap.  policy->seq,
- * flags, out_conf and out_gap are ignored; out_gap may be NULL.
+ * confidence, the candidate token and the top-2 logit gap, and with
+ * policy->topk > 0 the top-k export.  policy->seq, flags, out_conf and
+ * out_gap are ignored; out_gap may be NULL.
  */
 int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* policy,
                     float* out_conf, int32_t* out_tokens, float* out_gap);
@@ -172,13 +195,17 @@ int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* p
  * Commit policies only, from given per-row confidences and candidates
  * (conf [B][L] float, tokens [B][L] int32, device).  Same state semantics as
  * dlm_decode_step; out_tokens of that call equals `tokens` here.  policy->H,
- * V, dtype, workspace, out_conf and out_gap are ignored.
+ * V, dtype, workspace, out_conf, out_gap and the top-k fields are ignored.
  */
 int dlm_commit(const float* conf, const int32_t* tokens, uint8_t* mask_state,
                dlm_credit_slot* credit_state, const dlm_policy* policy, uint8_t* out_commit);
 
 /* Workspace bytes a call with these shapes needs (0 if the shapes are unsupported). */
 size_t dlm_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype);
+
+/* Same for a call with policy->topk = topk (0 if unsupported or topk outside 0..DLM_MAX_TOPK);
+   topk = 0 gives dlm_workspace_bytes. */
+size_t dlm_workspace_bytes_topk(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int32_t topk);
 
 /* Zero-fill a workspace on `stream` (a fill kernel, safe under graph capture). */
 int dlm_workspace_init(void* workspace, size_t workspace_bytes, void* stream);

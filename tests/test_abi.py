@@ -44,13 +44,13 @@ def test_version_matches_header(lib):
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    for name in ["DLM_MAX_SEQS", "DLM_MAX_L", "DLM_CREDIT_SLOTS", "DLM_MAX_RULES"]:
+    for name in ["DLM_MAX_SEQS", "DLM_MAX_L", "DLM_CREDIT_SLOTS", "DLM_MAX_RULES", "DLM_MAX_TOPK"]:
         assert int(re.search(rf"#define {name} (\d+)", text).group(1)) == getattr(nat, name)
     for name in ["DLM_SEQ_RUNNING", "DLM_SEQ_FINISHED", "DLM_SEQ_EOS_IN_BLOCK"]:
         assert int(re.search(rf"{name} = (\d+)", text).group(1)) == getattr(nat, name)
     assert ctypes.sizeof(nat.dlm_credit_slot) == 8
     assert ctypes.sizeof(nat.dlm_seq_policy) == 20       # the library asserts the same sizes
-    assert ctypes.sizeof(nat.dlm_policy) == 96
+    assert ctypes.sizeof(nat.dlm_policy) == 120
 
 
 def test_workspace_sizes():
@@ -71,9 +71,11 @@ def test_workspace_sizes():
         assert nat.dlm_workspace_bytes(*bad) == 0, bad
 
 
-def policy(B=1, L=8, H=64, V=1024, dtype=nat.DLM_BF16, seq=None, ws=FAKE, ws_bytes=1 << 20, flags=0):
+def policy(B=1, L=8, H=64, V=1024, dtype=nat.DLM_BF16, seq=None, ws=FAKE, ws_bytes=1 << 20, flags=0, topk=0,
+           topk_tokens=FAKE):
     seq = seq if seq is not None else [(nat.DLM_THRESHOLD, 0.9, 0.0, 0)] * B
-    return nat.StepPolicy(B, L, H, V, dtype, seq, workspace=ws, workspace_bytes=ws_bytes, flags=flags)
+    return nat.StepPolicy(B, L, H, V, dtype, seq, workspace=ws, workspace_bytes=ws_bytes, flags=flags, topk=topk,
+                          out_topk_tokens=topk_tokens if topk else None)
 
 
 def status_of(fn, *args):
@@ -188,6 +190,35 @@ def test_decode_steps_validation():
     assert steps(policy(L=65)) == nat.DLM_ERR_SHAPE
     assert steps(policy(seq=[(7, 0.9, 0, 0)])) == nat.DLM_ERR_POLICY
     assert nat.load().dlm_decode_steps(FAKE, FAKE, FAKE, FAKE, None, 2, FAKE, FAKE) == nat.DLM_ERR_NULL
+
+
+def test_topk_workspace_sizes():
+    # top-k on: the streaming plan for every shape, plus one list of 8 (logit, id) pairs (64 bytes)
+    # per (padded row, vocabulary range) after the statistics records
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 8) == 256 + 32 * 256 * 16 + 32 * 256 * 64
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 3) == 256 + 32 * 256 * 16 + 32 * 256 * 64
+    # 512 bf16 rows: 64-row groups (8 of them), 32 vocabulary ranges each, no packed hidden rows
+    assert nat.dlm_workspace_bytes_topk(16, 32, 2048, 157184, nat.DLM_BF16, 8) == 256 + 512 * 32 * 16 + 512 * 32 * 64
+    for B, L, H, V, dt in [(1, 32, 2048, 126464, 1), (16, 32, 2048, 157184, 1), (1, 8, 64, 1024, 0)]:
+        assert nat.dlm_workspace_bytes_topk(B, L, H, V, dt, 0) == nat.dlm_workspace_bytes(B, L, H, V, dt)
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 9) == 0
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, -1) == 0
+    assert nat.dlm_workspace_bytes_topk(0, 32, 2048, 126464, nat.DLM_BF16, 4) == 0
+
+
+def test_topk_validation():
+    need = nat.dlm_workspace_bytes_topk(1, 8, 64, 1024, nat.DLM_BF16, 4)
+    assert need > nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_BF16)
+    assert step(policy(ws_bytes=need, topk=9)) == nat.DLM_ERR_POLICY
+    assert step(policy(ws_bytes=need, topk=-2)) == nat.DLM_ERR_POLICY
+    assert step(policy(ws_bytes=need, topk=4, topk_tokens=None)) == nat.DLM_ERR_NULL
+    assert step(policy(ws_bytes=need - 1, topk=4)) == nat.DLM_ERR_WORKSPACE
+    small = nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_BF16)
+    assert status_of(nat.dlm_token_stats, FAKE, FAKE, policy(ws_bytes=small, topk=4), FAKE, FAKE) == nat.DLM_ERR_WORKSPACE
+    assert status_of(nat.dlm_token_stats, FAKE, FAKE, policy(ws_bytes=need, topk=99), FAKE, FAKE) == nat.DLM_ERR_POLICY
+    steps = lambda pol: status_of(nat.dlm_decode_steps, FAKE, FAKE, FAKE, FAKE, pol, 2, FAKE, FAKE)
+    assert steps(policy(ws_bytes=need, topk=4, topk_tokens=None)) == nat.DLM_ERR_NULL
+    assert steps(policy(ws_bytes=need, topk=12)) == nat.DLM_ERR_POLICY
 
 
 def test_binding_raises_without_library(tmp_path):
