@@ -33,7 +33,7 @@ MFMA_FP32_PEAK_TFLOPS = 157.3
 METRIC = "decode-step positions/sec (LM head+confidence+commit), B=1 L=32; % HBM/MFMA peak"
 
 
-def algorithmic_work(wl):
+def algorithmic_work(wl, topk=0):
     """Bytes the step must move and flops it must do (the [M][V] logits are never stored)."""
     es = 2 if wl.dtype == "bf16" else 4
     M = wl.B * wl.L
@@ -41,6 +41,7 @@ def algorithmic_work(wl):
     state = M * (1 + 1 + 4 + 1 + 4 + 4)            # mask in/out, tokens, commit, conf, gap
     if any_credit:
         state += 2 * M * 4 * 8                     # credit slots in/out
+    state += M * topk * 8                          # top-k tokens and probabilities
     bytes_ = wl.V * wl.H * es + M * wl.H * es + state
     flops = 2.0 * M * wl.V * wl.H
     return bytes_, flops
@@ -59,7 +60,7 @@ def measured_traffic(workload):
     return d.get("hbm_bytes_per_launch")
 
 
-def record_trajectory(wl, W, Wd, steps, dev):
+def record_trajectory(wl, W, Wd, steps, dev, topk=0):
     """Untimed: step once per input with host sync, recording the inputs each step consumed."""
     import numpy as np
     import torch
@@ -68,7 +69,7 @@ def record_trajectory(wl, W, Wd, steps, dev):
     from decoding_step_amd.synth import BlockStream
 
     seq = [(p.kind, p.threshold, p.decay, p.max_depth) for p in wl.policies]
-    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE)
+    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, topk=topk)
     streams = [BlockStream(W, wl.L, s, wl.a_max, rp) for s, rp in zip(wl.seeds, wl.redraw_p)]
     pos = [[0, 0] for _ in range(wl.B)]
     mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
@@ -87,24 +88,26 @@ def record_trajectory(wl, W, Wd, steps, dev):
     return hidden, seq, commits, blocks_done
 
 
-def time_steps_device_loop(wl, Wd, hidden, seq, warmup, steps, dev, graph):
+def time_steps_device_loop(wl, Wd, hidden, seq, warmup, steps, dev, graph, topk=0):
     """All timed steps in one dlm_decode_steps call (optionally captured once as a graph and replayed)."""
     import torch
     from decoding_step_amd import _native as nat
     from decoding_step_amd.device import Decoder, new_credit
 
     stream = torch.cuda.Stream(dev) if graph else torch.cuda.current_stream(dev)
-    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream)
+    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream, topk=topk)
     mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
     credit = new_credit(wl.B, wl.L, dev)
     credit0 = credit.clone()
     tok = torch.empty((steps, wl.B, wl.L), dtype=torch.int32, device=dev)
     com = torch.empty((steps, wl.B, wl.L), dtype=torch.uint8, device=dev)
+    tk_tok = torch.empty((steps, wl.B, wl.L, topk), dtype=torch.int32, device=dev) if topk else None
+    tk_prob = torch.empty((steps, wl.B, wl.L, topk), dtype=torch.float32, device=dev) if topk else None
+    run = lambda: dec.steps(hidden[:steps], mask, credit, tok, com, tk_tok, tk_prob)
     with torch.cuda.stream(stream):
         for _ in range(max(1, warmup // max(1, steps))):
-            dec.steps(hidden[:steps], mask, credit, tok, com)
+            run()
     torch.cuda.synchronize()
-    run = lambda: dec.steps(hidden[:steps], mask, credit, tok, com)
     if graph:
         g = torch.cuda.CUDAGraph()
         mask.fill_(1)
@@ -129,7 +132,7 @@ def time_steps_device_loop(wl, Wd, hidden, seq, warmup, steps, dev, graph):
     return ev0.elapsed_time(ev1) / 1e3, wall, None
 
 
-def time_steps(wl, Wd, hidden, seq, warmup, steps, dev):
+def time_steps(wl, Wd, hidden, seq, warmup, steps, dev, topk=0):
     """One dlm_decode_step call per step.  The region is timed with two events only; a second
     pass over the same steps records an event between consecutive steps for the per-step
     distribution (those events add ~3 us to each step, so the rate comes from the first pass)."""
@@ -138,7 +141,7 @@ def time_steps(wl, Wd, hidden, seq, warmup, steps, dev):
     from decoding_step_amd.device import Decoder, new_credit
 
     stream = torch.cuda.current_stream(dev)
-    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream)
+    dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream, topk=topk)
     mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
     credit = new_credit(wl.B, wl.L, dev)
     credit0 = credit.clone()
@@ -172,8 +175,9 @@ def time_steps(wl, Wd, hidden, seq, warmup, steps, dev):
     return total, wall, per_step
 
 
-def cpu_baseline(wl, W, budget_s=20.0):
-    """The oracle as it stands, on the first steps of the same workload, on this host's cores."""
+def cpu_baseline(wl, W, budget_s=20.0, topk=0):
+    """The oracle as it stands, on the first steps of the same workload, on this host's cores
+    (with the top-k export, the oracle's topk_candidates over the same rows is part of a step)."""
     import numpy as np
     import oracle
     from decoding_step_amd.synth import BlockStream
@@ -191,6 +195,8 @@ def cpu_baseline(wl, W, budget_s=20.0):
         h = np.stack([streams[b].hidden(*pos[b]) for b in range(wl.B)])
         t0 = time.perf_counter()
         out = oracle.decode_step(h, W, mask, seq, ctok, cval, auto_advance=True)
+        if topk:
+            oracle.topk_candidates(h, W, topk)
         t += time.perf_counter() - t0
         mask, ctok, cval = out["mask"], out["credit_tok"], out["credit_val"]
         for b in range(wl.B):
@@ -202,6 +208,8 @@ def cpu_baseline(wl, W, budget_s=20.0):
         t1 = time.perf_counter()
         oracle.decode_step(h, W, np.ones((wl.B, wl.L), np.uint8), seq, np.full((wl.B, wl.L, 4), -1, np.int32),
                            np.zeros((wl.B, wl.L, 4), np.float32), auto_advance=True)
+        if topk:
+            oracle.topk_candidates(h, W, topk)
         t1 = time.perf_counter() - t1
     model = ""
     try:
@@ -225,7 +233,11 @@ def main():
                     help="one dlm_decode_step call per step (default), all timed steps in one "
                          "dlm_decode_steps call, or that call captured as a graph and replayed")
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="also export the k best candidates of every row (0 = off, at most 8)")
     args = ap.parse_args()
+    if not 0 <= args.topk <= 8:
+        ap.error("--topk must be in 0..8")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the step shards by sequence or by vocabulary range; see the design notes).", file=sys.stderr)
@@ -249,15 +261,15 @@ def main():
     Wd = to_device(W, dev)
     n_in = max(args.steps, 1)
     print(f"[bench] recording {n_in} steps", file=sys.stderr, flush=True)
-    hidden, seq, commits, blocks = record_trajectory(wl, W, Wd, n_in, dev)
+    hidden, seq, commits, blocks = record_trajectory(wl, W, Wd, n_in, dev, args.topk)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
     if args.loop == "calls":
-        t, wall, per_step = time_steps(wl, Wd, hidden, seq, args.warmup, args.steps, dev)
+        t, wall, per_step = time_steps(wl, Wd, hidden, seq, args.warmup, args.steps, dev, args.topk)
     else:
         t, wall, per_step = time_steps_device_loop(wl, Wd, hidden, seq, args.warmup, args.steps, dev,
-                                                   graph=args.loop == "graph")
+                                                   graph=args.loop == "graph", topk=args.topk)
     ms = t / args.steps * 1e3
-    bytes_, flops = algorithmic_work(wl)
+    bytes_, flops = algorithmic_work(wl, args.topk)
     sec_per_step = t / args.steps
     if flops / bytes_ > 312 and wl.dtype == "bf16":
         roof = {"bound": "mfma", "achieved": flops / sec_per_step / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
@@ -265,8 +277,11 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": bytes_ / sec_per_step / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(wl.name)
-    if wl.dtype == "bf16" and wl.B * wl.L > 64 and wl.H % 256 == 0:   # GEMM-shaped path
+    roof["traffic"] = measured_traffic(wl.name + (f"_topk{args.topk}" if args.topk else ""))
+    if args.topk:
+        roof["kernel"] = ("dlm::step_kernel with the top-k fold (the timed step also holds "
+                          "finalize_topk_kernel)")
+    elif wl.dtype == "bf16" and wl.B * wl.L > 64 and wl.H % 256 == 0:   # GEMM-shaped path
         roof["kernel"] = "dlm::gemm_wide_kernel (the timed step also holds pack_hidden_kernel and finalize_kernel)"
     else:
         roof["kernel"] = "dlm::step_kernel (one launch per step)"
@@ -279,7 +294,8 @@ def main():
         "data": "synthetic (seeded generator: W ~ N(0,0.02), planted-peak hidden states)",
         "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "H": wl.H, "V": wl.V,
                    "policies": sorted(set(f"{['threshold', 'hierarchical', 'credit'][p.kind]} {p.threshold}"
-                                          for p in wl.policies))},
+                                          for p in wl.policies)),
+                   "topk": args.topk},
         "roofline": roof,
         "step_us": None if per_step is None else {
             "median": float(np.median(per_step)), "p10": float(np.percentile(per_step, 10)),
@@ -293,7 +309,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(wl, W, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(wl, W, args.cpu_budget, args.topk)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -1214,35 +1214,18 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, 
   finalize_sequences(c, rec, G, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
-// Top-k export of one row (one wavefront): the G best-first lists of the row (lists g = lane,
-// lane + 64, ... per lane) are merged by taking the best head kTopK times, lowest id among equal
-// logits.  A candidate's probability is 2^((z - M) log2 e) / S with the row's maximum M and sum S,
-// so entry 0 equals the row's confidence.
-__device__ __forceinline__ void topk_finalize_row(const CommitArgs& c, __amdgpu_buffer_rsrc_t trec, int G, int row,
-                                                  float M, float inv_s) {
-  constexpr int N = kMaxVocabGroups / 64;
+// Top-k export of one row (one wavefront).  Lane l holds the row's best-first lists g = l, l + 64,
+// ... (empty past G).  Each round the wave takes the best head (largest logit, then lowest id);
+// only the lane that held it pops that list and re-scans its heads, inside a branch, so a round
+// costs two wave reductions and one lane's update.  A candidate's probability is
+// 2^((z - M) log2 e) / S with the row's maximum M and sum S, so entry 0 equals the confidence.
+template <int N>
+__device__ __forceinline__ void topk_merge_row(const CommitArgs& c, TopK (&t)[N], int row, float M, float inv_s) {
   const int lane = __lane_id();
-  TopK t[N];
-  const unsigned base = (unsigned)row * (unsigned)G * (kTopK * 8u);
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const int g = lane + 64 * n;
-    topk_clear(t[n]);
-    if (g < G) {
-#pragma unroll
-      for (int j = 0; j < kTopK / 2; ++j) {
-        const float4 e = record_load(trec, base + (unsigned)g * (kTopK * 8u) + 16u * j);
-        t[n].z[2 * j] = e.x;
-        t[n].id[2 * j] = __float_as_int(e.y);
-        t[n].z[2 * j + 1] = e.z;
-        t[n].id[2 * j + 1] = __float_as_int(e.w);
-      }
-    }
-  }
-  const size_t out0 = (size_t)row * c.topk;
-  for (int r = 0; r < c.topk; ++r) {
-    float bz = t[0].z[0];
-    int bi = t[0].id[0], bn = 0;
+  auto best_head = [&](float& bz, int& bi, int& bn) {
+    bz = t[0].z[0];
+    bi = t[0].id[0];
+    bn = 0;
 #pragma unroll
     for (int n = 1; n < N; ++n) {
       const bool better = t[n].z[0] > bz || (t[n].z[0] == bz && t[n].id[0] < bi);
@@ -1250,11 +1233,20 @@ __device__ __forceinline__ void topk_finalize_row(const CommitArgs& c, __amdgpu_
       bi = better ? t[n].id[0] : bi;
       bn = better ? n : bn;
     }
+  };
+  float bz;
+  int bi, bn;
+  best_head(bz, bi, bn);
+  const size_t out0 = (size_t)row * c.topk;
+  for (int r = 0; r < c.topk; ++r) {
     const float m = wave_max(bz);
     const int id = wave_allreduce_min(bz == m ? bi : kNoToken);
-    const bool win = bz == m && bi == id;
+    if (bz == m && bi == id && id != kNoToken) {   // the one lane holding the winner
 #pragma unroll
-    for (int n = 0; n < N; ++n) topk_pop_if(t[n], win && bn == n);
+      for (int n = 0; n < N; ++n)
+        if (bn == n) topk_pop_if(t[n], true);
+      best_head(bz, bi, bn);
+    }
     if (lane == 0) {
       const bool real = id != kNoToken;
       c.out_topk_tokens[out0 + r] = real ? id : -1;
@@ -1266,9 +1258,12 @@ __device__ __forceinline__ void topk_finalize_row(const CommitArgs& c, __amdgpu_
 // Merge + commit after the streaming kernel with the top-k fold.  Workgroups [0, B) merge and
 // commit one sequence each, as finalize_kernel; the others take one row per wavefront: they merge
 // its statistics records again (same order, same result) for M and S, then its top-k records.
+// Every load of a row is issued before the first wait (records past G read as out of range and
+// are replaced by empty values), so a row costs one round trip to memory.
 __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArgs c, const float4* records,
                                                                  const float4* topk_records, int G,
                                                                  int nrows_total) {
+  constexpr int N = kMaxVocabGroups / 64;
   __shared__ uint4 stage[kRowsPerStage / 2];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const __amdgpu_buffer_rsrc_t rec =
@@ -1284,16 +1279,34 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
   const int row = ((int)blockIdx.x - c.B) * kWaves + wave;
   if (row >= c.B * c.L) return;
   const int lane = threadIdx.x & 63;
-  float4 r[kMaxVocabGroups / 64];
-#pragma unroll
-  for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
-    const int g = lane + 64 * i;
-    r[i] = g < G ? record_load(rec, (unsigned)(((size_t)row * G + g) * 16)) : stats_pack(stats_empty());
-  }
-  const Stats t = merge_records(r);
   const __amdgpu_buffer_rsrc_t trec = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float4*>(topk_records), 0, nrows_total * G * (kTopK * 8), 0x00020000);
-  topk_finalize_row(c, trec, G, row, t.m1, 1.f / t.s);
+  constexpr unsigned kOOB = 0x80000000u;   // beyond any range: the load returns zeros
+  float4 r[N];
+  float4 e[N][kTopK / 2];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int g = lane + 64 * n;
+    r[n] = record_load(rec, g < G ? (unsigned)(((size_t)row * G + g) * 16) : kOOB);
+#pragma unroll
+    for (int j = 0; j < kTopK / 2; ++j)
+      e[n][j] = record_load(trec, g < G ? (unsigned)(((size_t)row * G + g) * (kTopK * 8) + 16 * j) : kOOB);
+  }
+  TopK t[N];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const bool in = lane + 64 * n < G;
+    r[n] = in ? r[n] : stats_pack(stats_empty());
+#pragma unroll
+    for (int j = 0; j < kTopK / 2; ++j) {
+      t[n].z[2 * j] = in ? e[n][j].x : -INFINITY;
+      t[n].id[2 * j] = in ? __float_as_int(e[n][j].y) : kNoToken;
+      t[n].z[2 * j + 1] = in ? e[n][j].z : -INFINITY;
+      t[n].id[2 * j + 1] = in ? __float_as_int(e[n][j].w) : kNoToken;
+    }
+  }
+  const Stats st = merge_records(r);
+  topk_merge_row<N>(c, t, row, st.m1, 1.f / st.s);
 }
 
 // dlm_commit: conf / tokens given, one wavefront per sequence.

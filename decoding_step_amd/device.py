@@ -74,12 +74,16 @@ class Decoder:
     def steps(self, hidden_steps: torch.Tensor, mask: torch.Tensor, credit, out_tokens: torch.Tensor,
               out_commit: torch.Tensor, out_topk_tokens=None, out_topk_prob=None) -> None:
         """hidden_steps[n] for step n; per-step outputs [n][B][L] (dlm_decode_steps), and with top-k on
-        per-step exports [n][B][L][topk] (the Decoder's own single-step buffers when not given)."""
-        if self.topk and out_topk_tokens is not None:
+        per-step exports [n][B][L][topk] (required: the library writes one export per step)."""
+        n = hidden_steps.shape[0]
+        if self.topk:
+            if out_topk_tokens is None or out_topk_tokens.numel() < n * self.B * self.L * self.topk:
+                raise ValueError(f"top-k is on: out_topk_tokens must hold [{n}][{self.B}][{self.L}][{self.topk}]")
+            if out_topk_prob is not None and out_topk_prob.numel() < n * self.B * self.L * self.topk:
+                raise ValueError(f"out_topk_prob must hold [{n}][{self.B}][{self.L}][{self.topk}]")
             self.policy.set_topk(self.topk, out_topk_tokens, out_topk_prob)
         try:
-            nat.dlm_decode_steps(hidden_steps, self.W, mask, credit, self.policy, hidden_steps.shape[0], out_tokens,
-                                 out_commit)
+            nat.dlm_decode_steps(hidden_steps, self.W, mask, credit, self.policy, n, out_tokens, out_commit)
         finally:
             if self.topk:
                 self.policy.set_topk(self.topk, self.topk_tokens, self.topk_prob)

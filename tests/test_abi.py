@@ -221,6 +221,24 @@ def test_topk_validation():
     assert steps(policy(ws_bytes=need, topk=12)) == nat.DLM_ERR_POLICY
 
 
+def test_decoder_steps_needs_per_step_topk_buffers():
+    # with the export on, dlm_decode_steps writes one [B][L][k] export per step: the Decoder
+    # refuses buffers that cannot hold them instead of passing its single-step ones
+    torch = pytest.importorskip("torch")
+    from decoding_step_amd.device import Decoder
+    W = torch.zeros((1024, 64), dtype=torch.bfloat16)
+    dec = Decoder(W, 1, 8, [(nat.DLM_THRESHOLD, 0.9, 0.0, 0)], topk=4)
+    assert dec.workspace.numel() == nat.dlm_workspace_bytes_topk(1, 8, 64, 1024, nat.DLM_BF16, 4)
+    hs = torch.zeros((3, 1, 8, 64), dtype=torch.bfloat16)
+    out_t = torch.zeros((3, 1, 8), dtype=torch.int32)
+    out_c = torch.zeros((3, 1, 8), dtype=torch.uint8)
+    with pytest.raises(ValueError, match="top-k is on"):
+        dec.steps(hs, torch.ones((1, 8), dtype=torch.uint8), None, out_t, out_c)
+    with pytest.raises(ValueError, match="top-k is on"):
+        dec.steps(hs, torch.ones((1, 8), dtype=torch.uint8), None, out_t, out_c,
+                  torch.zeros((2, 1, 8, 4), dtype=torch.int32))
+
+
 def test_binding_raises_without_library(tmp_path):
     saved = nat._lib
     try:
