@@ -9,7 +9,7 @@ See :mod:`oracle.reference` for the definitions and the pages they follow.
 """
 from .reference import (  # noqa: F401
     THRESHOLD, HIERARCHICAL, CREDIT, SLOTS,
-    as_f64, lm_head_logits, token_stats, topk_candidates,
+    as_f64, lm_head_logits, token_stats, topk_candidates, shard_stats, merge_shards,
     commit_threshold, commit_hierarchical, commit_credit,
     RUNNING, FINISHED, EOS_IN_BLOCK, early_stop,
     decode_step,

@@ -134,6 +134,64 @@ def token_stats(hidden: np.ndarray, W: np.ndarray, row_chunk: int = 64) -> dict:
     return {"conf": conf.reshape(shape), "tok": tok.reshape(shape), "gap": gap.reshape(shape)}
 
 
+def shard_stats(hidden: np.ndarray, W_shard: np.ndarray, v_begin: int, row_chunk: int = 64) -> dict:
+    """Softmax statistics of every row over one vocabulary shard (tokens ``v_begin ..
+    v_begin + V_shard - 1``), the per-GPU half of the tensor-parallel head (explainer,
+    system-level optimisations: the model is split over GPUs so a single request uses them all).
+
+    * ``m``: the largest logit of the shard (float64), ``s = sum exp(z - m)`` over the shard;
+    * ``tok``: the lowest global id among the shard's float32-rounded maxima (R2), ``top32`` that
+      float32 maximum, ``second32`` the shard's second-largest float32 logit (with multiplicity).
+    """
+    hidden = np.asarray(hidden)
+    H = W_shard.shape[1]
+    h2 = hidden.reshape(-1, H)
+    M = h2.shape[0]
+    out = {"m": np.empty(M), "s": np.empty(M), "tok": np.empty(M, np.int64),
+           "top32": np.empty(M, np.float32), "second32": np.empty(M, np.float32)}
+    for r0 in range(0, M, row_chunk):
+        z = lm_head_logits(h2[r0:r0 + row_chunk], W_shard)
+        n = z.shape[0]
+        rows = np.arange(n)
+        z32 = z.astype(np.float32)
+        t = np.argmax(z32, axis=1)
+        rest = z32.copy()
+        rest[rows, t] = -np.inf
+        m = z.max(axis=1)
+        out["m"][r0:r0 + n] = m
+        out["s"][r0:r0 + n] = np.exp(z - m[:, None]).sum(axis=1)
+        out["tok"][r0:r0 + n] = v_begin + t
+        out["top32"][r0:r0 + n] = z32[rows, t]
+        out["second32"][r0:r0 + n] = rest.max(axis=1) if z.shape[1] > 1 else -np.inf
+    return out
+
+
+def merge_shards(shards: Sequence[dict]) -> dict:
+    """Statistics of the whole vocabulary from the shards' (in vocabulary order): the exchange
+    step of the tensor-parallel head.  ``M = max m``, ``S = sum s_g exp(m_g - M)``, ``conf = 1/S``;
+    the candidate is the lowest id among the shards whose float32 maximum is the largest; the
+    runner-up logit is the larger of that shard's own runner-up and every other shard's maximum."""
+    m = np.stack([d["m"] for d in shards])
+    s = np.stack([d["s"] for d in shards])
+    top = np.stack([d["top32"] for d in shards])
+    sec = np.stack([d["second32"] for d in shards])
+    tok = np.stack([d["tok"] for d in shards])
+    G, M = m.shape
+    Mx = m.max(axis=0)
+    S = (s * np.exp(m - Mx[None, :])).sum(axis=0)
+    conf = (1.0 / S).astype(np.float32)
+    T = top.max(axis=0)
+    out_tok = np.empty(M, np.int64)
+    gap = np.empty(M, np.float32)
+    for r in range(M):
+        winners = [g for g in range(G) if top[g, r] == T[r]]
+        w = min(winners, key=lambda g: tok[g, r])
+        out_tok[r] = tok[w, r]
+        second = max([float(sec[w, r])] + [float(top[g, r]) for g in range(G) if g != w])
+        gap[r] = np.float32(float(T[r]) - second)
+    return {"conf": conf, "tok": out_tok, "gap": gap}
+
+
 def topk_candidates(hidden: np.ndarray, W: np.ndarray, k: int, row_chunk: int = 64) -> dict:
     """The ``k`` best candidates of every row and their softmax probabilities.
 
