@@ -21,7 +21,7 @@ DLM_F32, DLM_BF16 = 0, 1
 DLM_THRESHOLD, DLM_HIERARCHICAL, DLM_CREDIT = 0, 1, 2
 DLM_AUTO_ADVANCE = 1
 DLM_SEQ_RUNNING, DLM_SEQ_FINISHED, DLM_SEQ_EOS_IN_BLOCK = 0, 1, 2
-DLM_MAX_SEQS, DLM_MAX_L, DLM_CREDIT_SLOTS, DLM_MAX_RULES, DLM_MAX_TOPK = 256, 64, 4, 8, 8
+DLM_MAX_SEQS, DLM_MAX_L, DLM_CREDIT_SLOTS, DLM_MAX_RULES, DLM_MAX_TOPK, DLM_MAX_SHARDS = 256, 64, 4, 8, 8, 256
 
 STATUS_NAMES = {0: "DLM_OK", -1: "DLM_ERR_NULL", -2: "DLM_ERR_DTYPE", -3: "DLM_ERR_SHAPE",
                 -4: "DLM_ERR_POLICY", -5: "DLM_ERR_WORKSPACE", -6: "DLM_ERR_HIP"}
@@ -29,6 +29,11 @@ STATUS_NAMES = {0: "DLM_OK", -1: "DLM_ERR_NULL", -2: "DLM_ERR_DTYPE", -3: "DLM_E
 
 class dlm_credit_slot(ctypes.Structure):
     _fields_ = [("token", ctypes.c_int32), ("credit", ctypes.c_float)]
+
+
+class dlm_shard_record(ctypes.Structure):
+    _fields_ = [("max_logit", ctypes.c_float), ("sum_exp", ctypes.c_float), ("token", ctypes.c_int32),
+                ("second_logit", ctypes.c_float)]
 
 
 class dlm_seq_policy(ctypes.Structure):
@@ -74,6 +79,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dlm_token_stats.restype = ctypes.c_int
     lib.dlm_commit.argtypes = [vp, vp, vp, vp, pol, vp]
     lib.dlm_commit.restype = ctypes.c_int
+    lib.dlm_shard_stats.argtypes = [vp, vp, i64, pol, vp]
+    lib.dlm_shard_stats.restype = ctypes.c_int
+    lib.dlm_merge_commit.argtypes = [vp, i64, vp, vp, pol, vp, vp]
+    lib.dlm_merge_commit.restype = ctypes.c_int
     lib.dlm_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
     lib.dlm_workspace_bytes.restype = ctypes.c_size_t
     lib.dlm_workspace_bytes_topk.argtypes = [i64, i64, i64, i64, i32, i32]
@@ -183,6 +192,17 @@ def dlm_token_stats(hidden, W_vocab, policy: StepPolicy, out_conf, out_tokens, o
 def dlm_commit(conf, tokens, mask_state, credit_state, policy: StepPolicy, out_commit) -> None:
     _check(load().dlm_commit(_ptr(conf), _ptr(tokens), _ptr(mask_state), _ptr(credit_state),
                              ctypes.byref(policy.c), _ptr(out_commit)))
+
+
+def dlm_shard_stats(hidden, W_shard, v_begin: int, policy: StepPolicy, out_records) -> None:
+    """out_records: [B][L] dlm_shard_record, e.g. a float32 tensor [B][L][4] (max, sum, id bits, second)."""
+    _check(load().dlm_shard_stats(_ptr(hidden), _ptr(W_shard), int(v_begin), ctypes.byref(policy.c), _ptr(out_records)))
+
+
+def dlm_merge_commit(records, n_shards: int, mask_state, credit_state, policy: StepPolicy, out_tokens,
+                     out_commit) -> None:
+    _check(load().dlm_merge_commit(_ptr(records), int(n_shards), _ptr(mask_state), _ptr(credit_state),
+                                   ctypes.byref(policy.c), _ptr(out_tokens), _ptr(out_commit)))
 
 
 def dlm_workspace_bytes(B: int, L: int, H: int, V: int, dtype: int) -> int:

@@ -12,6 +12,7 @@
 #include "dlm.h"
 #include "dlm_device.hpp"
 
+static_assert(sizeof(dlm_shard_record) == 16, "a shard record is one 16-byte statistics record");
 static_assert(sizeof(dlm_seq_policy) == 20 && sizeof(dlm_policy) == 120 && sizeof(dlm_credit_slot) == 8,
               "C ABI struct layout (the Python binding mirrors it)");
 
@@ -360,6 +361,56 @@ int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* p
   c.out_conf = out_conf;
   c.out_gap = out_gap;
   return run_step(hidden, W_vocab, policy, c, false);
+}
+
+int dlm_shard_stats(const void* hidden, const void* W_shard, int64_t v_begin, const dlm_policy* policy,
+                    dlm_shard_record* out_records) {
+  if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");
+  if (!hidden || !W_shard || !out_records)
+    return fail(DLM_ERR_NULL, "hidden, W_shard and out_records must be non-NULL");
+  if (policy->topk != 0) return fail(DLM_ERR_POLICY, "topk=%d: the shard call has no top-k export", (int)policy->topk);
+  if (v_begin < 0 || v_begin + policy->V > 0x7fffffffll)
+    return fail(DLM_ERR_SHAPE, "v_begin=%lld: the shard's tokens must lie in [0, 2^31 - 1)", (long long)v_begin);
+  if (misaligned(out_records, 16)) return fail(DLM_ERR_SHAPE, "out_records must be 16-byte aligned");
+  dlm::CommitArgs c;
+  std::memset(&c, 0, sizeof c);
+  c.out_records = reinterpret_cast<float4*>(out_records);
+  c.v_begin = (int)v_begin;
+  return run_step(hidden, W_shard, policy, c, false);
+}
+
+int dlm_merge_commit(const dlm_shard_record* records, int64_t n_shards, uint8_t* mask_state,
+                     dlm_credit_slot* credit_state, const dlm_policy* policy, int32_t* out_tokens,
+                     uint8_t* out_commit) {
+  if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");
+  if (!records || !mask_state || !out_tokens || !out_commit)
+    return fail(DLM_ERR_NULL, "records, mask_state, out_tokens and out_commit must be non-NULL");
+  if (policy->B < 1 || policy->B > DLM_MAX_SEQS)
+    return fail(DLM_ERR_SHAPE, "B=%lld outside [1, %d]", (long long)policy->B, DLM_MAX_SEQS);
+  if (policy->L < 1 || policy->L > DLM_MAX_L)
+    return fail(DLM_ERR_SHAPE, "L=%lld outside [1, %d]", (long long)policy->L, DLM_MAX_L);
+  if (policy->V < 1) return fail(DLM_ERR_SHAPE, "V=%lld must be >= 1 (the full vocabulary)", (long long)policy->V);
+  if (n_shards < 1 || n_shards > DLM_MAX_SHARDS)
+    return fail(DLM_ERR_SHAPE, "n_shards=%lld outside [1, %d]", (long long)n_shards, DLM_MAX_SHARDS);
+  if (misaligned(records, 16)) return fail(DLM_ERR_SHAPE, "records must be 16-byte aligned");
+  dlm::CommitArgs c;
+  std::memset(&c, 0, sizeof c);
+  int rc = pack_rules(policy, true, credit_state, policy->V, &c);
+  if (rc) return rc;
+  c.mask = mask_state;
+  c.credit = credit_state;
+  c.out_tokens = out_tokens;
+  c.out_commit = out_commit;
+  c.out_conf = policy->out_conf;
+  c.out_gap = policy->out_gap;
+  c.B = (int)policy->B;
+  c.L = (int)policy->L;
+  c.flags = dlm::kFlagCommit | (policy->flags & DLM_AUTO_ADVANCE);
+  hipLaunchKernelGGL(dlm::merge_commit_kernel, dim3(c.B), dim3(dlm::kThreads), 0, static_cast<hipStream_t>(policy->stream),
+                     c, reinterpret_cast<const float4*>(records), (int)n_shards);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DLM_ERR_HIP, "merge kernel launch: %s", hipGetErrorString(e));
+  return ok();
 }
 
 int dlm_commit(const float* conf, const int32_t* tokens, uint8_t* mask_state, dlm_credit_slot* credit_state,

@@ -51,6 +51,8 @@ struct CommitArgs {
   int32_t* out_topk_tokens;  // [B*L][topk] top-k export, or null (topk == 0)
   float* out_topk_prob;      // [B*L][topk] or null
   int topk;
+  float4* out_records;       // vocabulary shard: [B*L] merged records (global ids) instead of conf / token
+  int v_begin;               // first global token id of the shard
   int B, L;
   unsigned flags;
   Rule rules[DLM_MAX_RULES];
@@ -562,14 +564,17 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 }
 
 // ----------------------------------------------------------------------------------------------
-// Final merge + commit of sequences [b_begin, b_end): row r's G records sit at r*G .. r*G+G-1 of
-// `rec`.  One wavefront per row (kRowBatch rows with all their loads in flight together) merges
-// the records in a fixed order; conf / token go to LDS, then one wavefront per sequence commits.
+// Final merge + commit of sequences [b_begin, b_end): record g of row r sits at index
+// r*rs_row + g*rs_g of `rec` (rs_row = G, rs_g = 1 for the records of one head's workgroups;
+// rs_row = 1, rs_g = B*L for gathered vocabulary shards).  One wavefront per row (kRowBatch rows
+// with all their loads in flight together) merges the records in a fixed order; conf / token go
+// to LDS, then one wavefront per sequence commits.  With c.out_records the merged record itself
+// is written instead (ids offset by c.v_begin) and nothing commits.
 // `pre` is the state this wavefront already fetched for sequence `pre_b` (or pre_b = -1).
 // Called by a whole workgroup; `smem` needs kRowsPerStage * 8 bytes.
 // ----------------------------------------------------------------------------------------------
-__device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t rec, int G, int b_begin, int b_end,
-                                   uint4* smem, const SeqState& pre, int pre_b) {
+__device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t rec, int G, int rs_row, int rs_g,
+                                   int b_begin, int b_end, uint4* smem, const SeqState& pre, int pre_b) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool do_commit = (c.flags & kFlagCommit) != 0;
@@ -584,11 +589,11 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
 #pragma unroll
       for (int j = 0; j < kRowBatch; ++j) {
         const int rr = rr0 + j;
-        const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * G * 16);
+        const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
 #pragma unroll
         for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
           const int g = lane + 64 * i;
-          buf[j][i] = g < G ? record_load(rec, src + 16u * g) : stats_pack(stats_empty());
+          buf[j][i] = g < G ? record_load(rec, src + 16u * (unsigned)(g * rs_g)) : stats_pack(stats_empty());
         }
       }
 #pragma unroll
@@ -598,7 +603,11 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
 #pragma unroll
         for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
         const Stats t = merge_records(row_stats);
-        if (rr < nrows && lane == 0) {
+        if (rr < nrows && lane == 0 && c.out_records) {
+          Stats o = t;
+          o.id = t.id + c.v_begin;
+          c.out_records[r_first + rr] = stats_pack(o);
+        } else if (rr < nrows && lane == 0) {
           const int row = r_first + rr;
           // S >= 1 in exact arithmetic (the top logit's own term is 1); the exponent of that
           // term carries the rounding of m*log2(e), so 1/S may land a few ulps above 1
@@ -841,7 +850,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  finalize_sequences(c, rec, a.G_v, 0, c.B, smem, pre, wave < c.B ? wave : -1);
+  finalize_sequences(c, rec, a.G_v, a.G_v, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1);
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -1211,7 +1220,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, 
   SeqState pre;
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   if (do_commit && wave == 0) pre = load_seq_state(c, b);
-  finalize_sequences(c, rec, G, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  finalize_sequences(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // Top-k export of one row (one wavefront).  Lane l holds the row's best-first lists g = l, l + 64,
@@ -1273,7 +1282,7 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
     SeqState pre;
     const bool do_commit = (c.flags & kFlagCommit) != 0;
     if (do_commit && wave == 0) pre = load_seq_state(c, b);
-    finalize_sequences(c, rec, G, b, b + 1, stage, pre, wave == 0 ? b : -1);
+    finalize_sequences(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
     return;
   }
   const int row = ((int)blockIdx.x - c.B) * kWaves + wave;
@@ -1307,6 +1316,20 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
   }
   const Stats st = merge_records(r);
   topk_merge_row<N>(c, t, row, st.m1, 1.f / st.s);
+}
+
+// Merge + commit of gathered vocabulary shards (records [G][B*L], shards in vocabulary order):
+// the same merge and commit as the single-GPU head's, one workgroup per sequence.
+__global__ __launch_bounds__(kThreads) void merge_commit_kernel(const CommitArgs c, const float4* records, int G) {
+  __shared__ uint4 stage[kRowsPerStage / 2];
+  const int b = blockIdx.x;
+  const int M = c.B * c.L;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rec =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, G * M * 16, 0x00020000);
+  SeqState pre;
+  if (wave == 0) pre = load_seq_state(c, b);
+  finalize_sequences(c, rec, G, 1, M, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // dlm_commit: conf / tokens given, one wavefront per sequence.

@@ -38,13 +38,14 @@
 extern "C" {
 #endif
 
-#define DLM_VERSION_STRING "0.3.0"
+#define DLM_VERSION_STRING "0.4.0"
 
 #define DLM_MAX_SEQS 256   /* sequences per call                                  */
 #define DLM_MAX_L 64       /* positions per block: one wavefront lane per position */
 #define DLM_CREDIT_SLOTS 4 /* tracked (token, credit) candidates per position      */
 #define DLM_MAX_RULES 8    /* distinct dlm_seq_policy values per call              */
 #define DLM_MAX_TOPK 8     /* candidates per row in the top-k export               */
+#define DLM_MAX_SHARDS 256 /* vocabulary shards one dlm_merge_commit call merges    */
 
 /* Status codes. */
 enum {
@@ -199,6 +200,50 @@ int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* p
  */
 int dlm_commit(const float* conf, const int32_t* tokens, uint8_t* mask_state,
                dlm_credit_slot* credit_state, const dlm_policy* policy, uint8_t* out_commit);
+
+/*
+ * Vocabulary-sharded head (tensor parallelism over the vocabulary).  The explainer splits the
+ * model over GPUs so that one request uses all of them; for the head, GPU g holds the contiguous
+ * vocabulary range of shard g and produces one record per row, the records of all shards are
+ * all-gathered (B*L * 16 bytes per GPU), and every GPU merges them identically and commits.
+ * These two calls are the per-GPU parts; the exchange between them is the caller's.
+ */
+typedef struct {
+  float max_logit;    /* largest logit over the shard                                      */
+  float sum_exp;      /* sum over the shard of exp(z - max_logit), >= 1                    */
+  int32_t token;      /* lowest GLOBAL token id attaining max_logit                        */
+  float second_logit; /* second-largest logit of the shard, with multiplicity (-inf if the
+                         shard has one token)                                              */
+} dlm_shard_record;   /* 16 bytes */
+
+/*
+ * One GPU's share: the LM head over W_shard = rows [v_begin, v_begin + policy->V) of the full
+ * vocabulary head, one record per row.
+ *   hidden       [B][L][H]   dtype
+ *   W_shard      [V][H]      dtype             policy->V = the shard's size
+ *   v_begin      first global token id of the shard: >= 0, v_begin + V <= 2^31 - 1
+ *   out_records  [B][L]      dlm_shard_record  16-byte aligned
+ * policy->seq, flags, out_conf, out_gap and seq_done are ignored; topk must be 0
+ * (DLM_ERR_POLICY otherwise).  Workspace: dlm_workspace_bytes(B, L, H, V_shard, dtype).
+ */
+int dlm_shard_stats(const void* hidden, const void* W_shard, int64_t v_begin, const dlm_policy* policy,
+                    dlm_shard_record* out_records);
+
+/*
+ * The merge + commit after the exchange: records [n_shards][B][L] (shard g's out_records, the
+ * shards in vocabulary order, as an all-gather leaves them) are merged per row in shard order by
+ * the same merge the single-GPU head applies to its workgroups' records (largest logit, rescaled
+ * sum, lowest id among the maxima, runner-up), then the commit policies run exactly as in
+ * dlm_decode_step (same state semantics, out_conf / out_gap / seq_done included).
+ *   n_shards     1..DLM_MAX_SHARDS (DLM_ERR_SHAPE otherwise)
+ *   records      16-byte aligned (DLM_ERR_SHAPE otherwise)
+ * policy->V is the FULL vocabulary (end tokens are checked against it); policy->H, dtype,
+ * workspace and the top-k fields are ignored.  Every GPU that merges the same records in the
+ * same order reaches the same mask, credit and outputs.
+ */
+int dlm_merge_commit(const dlm_shard_record* records, int64_t n_shards, uint8_t* mask_state,
+                     dlm_credit_slot* credit_state, const dlm_policy* policy, int32_t* out_tokens,
+                     uint8_t* out_commit);
 
 /* Workspace bytes a call with these shapes needs (0 if the shapes are unsupported). */
 size_t dlm_workspace_bytes(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype);

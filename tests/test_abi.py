@@ -44,11 +44,12 @@ def test_version_matches_header(lib):
 
 def test_header_constants_match_binding():
     text = open(HEADER).read()
-    for name in ["DLM_MAX_SEQS", "DLM_MAX_L", "DLM_CREDIT_SLOTS", "DLM_MAX_RULES", "DLM_MAX_TOPK"]:
+    for name in ["DLM_MAX_SEQS", "DLM_MAX_L", "DLM_CREDIT_SLOTS", "DLM_MAX_RULES", "DLM_MAX_TOPK", "DLM_MAX_SHARDS"]:
         assert int(re.search(rf"#define {name} (\d+)", text).group(1)) == getattr(nat, name)
     for name in ["DLM_SEQ_RUNNING", "DLM_SEQ_FINISHED", "DLM_SEQ_EOS_IN_BLOCK"]:
         assert int(re.search(rf"{name} = (\d+)", text).group(1)) == getattr(nat, name)
     assert ctypes.sizeof(nat.dlm_credit_slot) == 8
+    assert ctypes.sizeof(nat.dlm_shard_record) == 16
     assert ctypes.sizeof(nat.dlm_seq_policy) == 20       # the library asserts the same sizes
     assert ctypes.sizeof(nat.dlm_policy) == 120
 
@@ -237,6 +238,37 @@ def test_decoder_steps_needs_per_step_topk_buffers():
     with pytest.raises(ValueError, match="top-k is on"):
         dec.steps(hs, torch.ones((1, 8), dtype=torch.uint8), None, out_t, out_c,
                   torch.zeros((2, 1, 8, 4), dtype=torch.int32))
+
+
+def test_shard_calls_validation():
+    need = nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_BF16)
+    p = policy(ws_bytes=need)
+    shard = lambda pol, hidden=FAKE, W=FAKE, v0=0, out=FAKE: status_of(nat.dlm_shard_stats, hidden, W, v0, pol, out)
+    assert shard(p, hidden=None) == nat.DLM_ERR_NULL
+    assert shard(p, W=None) == nat.DLM_ERR_NULL
+    assert shard(p, out=None) == nat.DLM_ERR_NULL
+    assert shard(p, v0=-1) == nat.DLM_ERR_SHAPE
+    assert shard(p, v0=(1 << 31) - 1024) == nat.DLM_ERR_SHAPE       # the shard's last id would overflow
+    assert shard(p, out=MISALIGNED) == nat.DLM_ERR_SHAPE
+    assert shard(policy(ws_bytes=need, topk=2)) == nat.DLM_ERR_POLICY
+    assert shard(policy(ws_bytes=need - 1)) == nat.DLM_ERR_WORKSPACE
+    assert shard(policy(L=65)) == nat.DLM_ERR_SHAPE
+    assert nat.load().dlm_shard_stats(FAKE, FAKE, 0, None, FAKE) == nat.DLM_ERR_NULL
+    merge = lambda pol, rec=FAKE, g=8, mask=FAKE, credit=FAKE, tok=FAKE, com=FAKE: status_of(
+        nat.dlm_merge_commit, rec, g, mask, credit, pol, tok, com)
+    assert merge(p, rec=None) == nat.DLM_ERR_NULL
+    assert merge(p, mask=None) == nat.DLM_ERR_NULL
+    assert merge(p, tok=None) == nat.DLM_ERR_NULL
+    assert merge(p, com=None) == nat.DLM_ERR_NULL
+    assert merge(p, g=0) == nat.DLM_ERR_SHAPE
+    assert merge(p, g=257) == nat.DLM_ERR_SHAPE
+    assert merge(p, rec=MISALIGNED) == nat.DLM_ERR_SHAPE
+    assert merge(policy(L=65)) == nat.DLM_ERR_SHAPE
+    assert merge(policy(B=0, seq=[])) == nat.DLM_ERR_SHAPE
+    assert merge(policy(seq=[(9, 0.9, 0, 0)])) == nat.DLM_ERR_POLICY
+    assert merge(policy(seq=[(2, 1.2, 0.7, 0)]), credit=None) == nat.DLM_ERR_NULL
+    assert merge(policy(seq=[(0, 0.9, 0, 0, 1024)])) == nat.DLM_ERR_POLICY      # end token past V
+    assert nat.load().dlm_merge_commit(FAKE, 2, FAKE, FAKE, None, FAKE, FAKE) == nat.DLM_ERR_NULL
 
 
 def test_binding_raises_without_library(tmp_path):
