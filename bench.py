@@ -175,6 +175,61 @@ def time_steps(wl, Wd, hidden, seq, warmup, steps, dev, topk=0):
     return total, wall, per_step
 
 
+def time_shard_share(wl, W, hidden, seq, warmup, steps, dev, G):
+    """One GPU's share of a step of the head split over G vocabulary shards: dlm_shard_stats on a
+    V/G-row shard, then dlm_merge_commit over G record sets (the other G-1 sets come from the other
+    shards on the first input; the exchange that would deliver them is not part of this timing).
+    Returns (total seconds, shard-kernel seconds, merge seconds) from HIP events on the stream."""
+    import numpy as np
+    import torch
+    from decoding_step_amd import _native as nat
+    from decoding_step_amd.device import new_credit, to_device, torch_dtype_code
+
+    cuts = [wl.V * g // G for g in range(G + 1)]
+    M = wl.B * wl.L
+    stream = torch.cuda.current_stream(dev)
+    W_sh = [to_device(np.ascontiguousarray(W[a:b]), dev) for a, b in zip(cuts[:-1], cuts[1:])]
+    code = torch_dtype_code(W_sh[0])
+    pols = []
+    for (a, b), w in zip(zip(cuts[:-1], cuts[1:]), W_sh):
+        ws = torch.zeros(nat.dlm_workspace_bytes(wl.B, wl.L, wl.H, b - a, code), dtype=torch.uint8, device=dev)
+        pols.append(nat.StepPolicy(wl.B, wl.L, wl.H, b - a, code, seq, ws, stream=stream))
+    records = torch.empty((G, M, 4), dtype=torch.float32, device=dev)
+    for g in range(G):                                  # the records the exchange would deliver
+        nat.dlm_shard_stats(hidden[0], W_sh[g], cuts[g], pols[g], records[g])
+    merge = nat.StepPolicy(wl.B, wl.L, wl.H, wl.V, code, seq, flags=nat.DLM_AUTO_ADVANCE, stream=stream)
+    tok = torch.empty((wl.B, wl.L), dtype=torch.int32, device=dev)
+    com = torch.empty((wl.B, wl.L), dtype=torch.uint8, device=dev)
+    mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device=dev)
+    credit = new_credit(wl.B, wl.L, dev)
+
+    def one(s):
+        nat.dlm_shard_stats(hidden[s], W_sh[0], 0, pols[0], records[0])
+        nat.dlm_merge_commit(records, G, mask, credit, merge, tok, com)
+
+    for s in range(warmup):
+        one(s % hidden.shape[0])
+    mask.fill_(1)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    ev[0].record(stream)
+    for s in range(steps):
+        one(s)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    total = ev[0].elapsed_time(ev[1]) / 1e3
+    # the two kernels apart: the shard kernel alone over the same inputs, then the merge alone
+    ev[0].record(stream)
+    for s in range(steps):
+        nat.dlm_shard_stats(hidden[s], W_sh[0], 0, pols[0], records[0])
+    ev[1].record(stream)
+    for s in range(steps):
+        nat.dlm_merge_commit(records, G, mask, credit, merge, tok, com)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    return total, ev[0].elapsed_time(ev[1]) / 1e3, ev[1].elapsed_time(ev[2]) / 1e3, cuts[1] - cuts[0]
+
+
 def cpu_baseline(wl, W, budget_s=20.0, topk=0):
     """The oracle as it stands, on the first steps of the same workload, on this host's cores
     (with the top-k export, the oracle's topk_candidates over the same rows is part of a step)."""
@@ -235,9 +290,14 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--topk", type=int, default=0,
                     help="also export the k best candidates of every row (0 = off, at most 8)")
+    ap.add_argument("--shards", type=int, default=1,
+                    help="time one GPU's share of a head split over this many vocabulary shards "
+                         "(shard kernel + merge of the shards' records; the exchange is not timed)")
     args = ap.parse_args()
     if not 0 <= args.topk <= 8:
         ap.error("--topk must be in 0..8")
+    if not 1 <= args.shards <= 256 or (args.shards > 1 and args.topk):
+        ap.error("--shards must be in 1..256, and the shard calls have no top-k export")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the step shards by sequence or by vocabulary range; see the design notes).", file=sys.stderr)
@@ -263,6 +323,31 @@ def main():
     print(f"[bench] recording {n_in} steps", file=sys.stderr, flush=True)
     hidden, seq, commits, blocks = record_trajectory(wl, W, Wd, n_in, dev, args.topk)
     print(f"[bench] timing {args.steps} steps after {args.warmup} warm-up", file=sys.stderr, flush=True)
+    if args.shards > 1:
+        total, t_shard, t_merge, v_shard = time_shard_share(wl, W, hidden, seq, args.warmup, args.steps, dev,
+                                                             args.shards)
+        es = 2 if wl.dtype == "bf16" else 4
+        M = wl.B * wl.L
+        shard_bytes = v_shard * wl.H * es + M * wl.H * es + M * 16
+        per = total / args.steps
+        out = {
+            "metric": METRIC + " -- one GPU's share of a vocabulary-sharded step",
+            "value": M / per, "unit": "positions/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": per * 1e3, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": wl.dtype, "data": "synthetic (seeded generator: W ~ N(0,0.02), planted-peak hidden states)",
+            "config": {"workload": wl.name, "B": wl.B, "L": wl.L, "H": wl.H, "V": wl.V, "shards": args.shards,
+                       "shard_rows": v_shard,
+                       "share": "dlm_shard_stats on one shard + dlm_merge_commit over all shards' records; "
+                                "the all-gather between them is not timed"},
+            "roofline": {"bound": "hbm", "kernel": "dlm_shard_stats (shard-shaped LM head)",
+                         "achieved": shard_bytes / (t_shard / args.steps) / 1e9, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": shard_bytes / (t_shard / args.steps) / 1e9 / HBM_PEAK_GBS,
+                         "traffic": None, "algorithmic_bytes_per_launch": shard_bytes},
+            "shard_us": t_shard / args.steps * 1e6, "merge_commit_us": t_merge / args.steps * 1e6,
+            "cpu_baseline": None,
+        }
+        print(json.dumps(out), flush=True)
+        return
     if args.loop == "calls":
         t, wall, per_step = time_steps(wl, Wd, hidden, seq, args.warmup, args.steps, dev, args.topk)
     else:
