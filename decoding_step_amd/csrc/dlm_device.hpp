@@ -702,8 +702,13 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   };
 
   // ---- hidden fragments of this wavefront's K positions, in registers ------------------------
-  // rows past M and fragments past F read as zero (outside the buffer range)
+  // rows past M and fragments past F read as zero (outside the buffer range).  Hidden fragment j
+  // goes out just before W fragment j of the first tile: loads retire in issue order, so the
+  // first tile's MFMAs on fragment j wait for fragments 0..j only, and the rest of the hidden
+  // rows arrive while the W stream is already running.
   uint4 hreg[KFWM][NMB];
+  // ring slot u*KFWM + j always holds fragment j of a tile congruent to u modulo G
+  uint4 ring[RING];
   {
     const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(a.hidden), 0, a.M * (int)row_bytes, 0x00020000);
@@ -716,18 +721,16 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
         const unsigned off = row * row_bytes + (unsigned)kf * 64u + (lane >> 4) * 16u;
         hreg[j][mb] = buffer_load16(hrs, kf < F ? off : kOOB);
       }
+      ring[j] = buffer_load16(wrs, w_off(0, j));
+      __builtin_amdgcn_sched_barrier(0);  // slot order = issue order
     }
   }
-  // The hidden loads go out before the ring, so waiting for the oldest ring slot implies them.
-  __builtin_amdgcn_sched_barrier(0);
-  // ring slot u*KFWM + j always holds fragment j of a tile congruent to u modulo G
-  uint4 ring[RING];
 #pragma unroll
-  for (int u = 0; u < G; ++u)
+  for (int u = 1; u < G; ++u)
 #pragma unroll
     for (int j = 0; j < KFWM; ++j) {
       ring[u * KFWM + j] = buffer_load16(wrs, w_off(u, j));
-      __builtin_amdgcn_sched_barrier(0);  // slot order = issue order
+      __builtin_amdgcn_sched_barrier(0);
     }
 
   // ---- stream the tiles -------------------------------------------------------------------------
