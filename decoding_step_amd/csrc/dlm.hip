@@ -51,6 +51,9 @@ struct Plan {
   size_t packed_off = 0, packed_bytes = 0;  // GEMM path: fragment-ordered hidden rows in the workspace
   int topk = 0;      // streaming kernel with the top-k fold + finalize_topk_kernel
   size_t topk_off = 0;                      // top-k records in the workspace
+  int nq = 0;        // streaming kernel: groups of dlm::kGroup vocabulary ranges (two-level merge)
+  size_t ticket_bytes = kTicketBytes;       // completion counters: global, then [n_rg][nq] groups
+  size_t level2_off = 0;                    // second-level records [n_rg * rows][nq]
 };
 
 int elem_bytes(int32_t dtype) { return dtype == DLM_BF16 ? 2 : dtype == DLM_F32 ? 4 : 0; }
@@ -119,7 +122,13 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
   p->G_v = (int)G_v;
   p->ntiles = (int)ntiles;
   p->lds = dlm::lds_bytes(NMB);
-  p->ws = kTicketBytes + (size_t)n_rg * MR * G_v * 16;
+  // counters (global + one per group, padded to 256 bytes) | records [n_rg * MR][G_v] |
+  // second-level records [n_rg * MR][nq]
+  const int64_t nq = (G_v + dlm::kGroup - 1) / dlm::kGroup;
+  p->nq = (int)nq;
+  p->ticket_bytes = (size_t)((4 * (1 + n_rg * nq) + 255) / 256 * 256);
+  p->level2_off = p->ticket_bytes + (size_t)n_rg * MR * G_v * 16;
+  p->ws = p->level2_off + (size_t)n_rg * MR * nq * 16;
   if (topk) {
     // ticket | records [n_rg * MR][G_v] | top-k records [n_rg * MR][G_v] x DLM_MAX_TOPK x 8 bytes
     if (n_rg * MR * G_v * (DLM_MAX_TOPK * 8) >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large for top-k");
@@ -223,7 +232,10 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   a.hidden = hidden;
   a.W = W;
   a.ticket = static_cast<unsigned*>(pol->workspace);
-  a.partials = reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + kTicketBytes);
+  a.group_tickets = a.ticket + 1;
+  a.partials = reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.ticket_bytes);
+  a.level2 = reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.level2_off);
+  a.nq = p.nq;
   a.H = (int)pol->H;
   a.V = (int)pol->V;
   a.M = (int)(pol->B * pol->L);
@@ -240,7 +252,7 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     void* packed = static_cast<char*>(pol->workspace) + p.packed_off;
     const int pack_blocks = (int)std::min<size_t>((p.packed_bytes / 16 + 255) / 256, 1024);
     hipLaunchKernelGGL(dlm::pack_hidden_kernel, dim3(pack_blocks), dim3(256), 0, stream,
-                       static_cast<const uint4*>(hidden), static_cast<uint4*>(packed), a.M, a.H);
+                       static_cast<const uint4*>(hidden), static_cast<uint4*>(packed), a.M, a.H, pack_blocks * 256);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "pack kernel launch: %s", hipGetErrorString(e));
     dlm::GemmArgs g;
@@ -459,7 +471,7 @@ int dlm_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
   if (workspace_bytes == 0) return ok();
   const size_t blocks = std::min<size_t>(1024, (workspace_bytes + 16 * 256 - 1) / (16 * 256));
   hipLaunchKernelGGL(dlm::fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<uint8_t*>(workspace), workspace_bytes);
+                     static_cast<uint8_t*>(workspace), workspace_bytes, (int)blocks * 256);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DLM_ERR_HIP, "fill kernel launch: %s", hipGetErrorString(e));
   return ok();

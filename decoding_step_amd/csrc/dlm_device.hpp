@@ -24,6 +24,7 @@ constexpr int kPrefetch = 8;          // 16-byte W fragments in flight per lane 
 constexpr int kRowsPerStage = 1024;   // finalize: rows staged in LDS at a time
 constexpr int kRowBatch = 4;          // finalize: rows per wavefront with loads in flight together
 constexpr int kMaxVocabGroups = 256;  // vocabulary ranges (records per row) at most
+constexpr int kGroup = 16;            // records per first-level group of the cross-workgroup merge
 constexpr unsigned kFlagCommit = 1u << 16;  // internal: run the commit policies
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -83,6 +84,9 @@ struct StepArgs {
   int G_v;             // vocabulary ranges (multiple of 8)
   int ntiles;          // ceil(V / 16)
   float4* topk_records;  // top-k fold only: [n_rg * 16 * NMB][G_v] lists of kTopK (logit, id)
+  unsigned* group_tickets;  // [n_rg][nq] completion counters of the groups of kGroup ranges
+  float4* level2;        // [n_rg * 16 * NMB][nq] merged record of each (row, group of ranges)
+  int nq;                // groups of ranges: ceil(G_v / kGroup)
   CommitArgs c;
 };
 
@@ -96,6 +100,12 @@ struct Stats {
 };
 
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Work-item and work-group ids read straight from the hardware-initialised registers: the device
+// library's accessors behind threadIdx / blockIdx are not inlined into kernels built without IEEE
+// mode and would be real calls.
+__device__ __forceinline__ int lid() { return (int)__builtin_amdgcn_workitem_id_x(); }
+__device__ __forceinline__ int gid() { return (int)__builtin_amdgcn_workgroup_id_x(); }
 
 // ---- cross-lane exchange on a 64-lane wavefront -------------------------------------------------
 // Within a row of 16 lanes: DPP quad permutes and row mirrors.  Across rows: the gfx950 row-swap
@@ -301,34 +311,31 @@ __device__ __forceinline__ void stats_fold1(Stats& st, float z, int v) {
   st.m1 = mnew;
 }
 
-// Merge the records of one row held by a wavefront (record g = lane + 64*i) into one result:
-// the maximum first, then the rescaled sum and the lowest id attaining the maximum, then the
-// second-largest logit (the winning record's own runner-up, or another record's maximum).
-// Every lane ends with the result; the summation order is fixed.
+// Merge the records of one row held by a wavefront (record g = lane + 64*i) in a fixed two-level
+// tree: the groups of kGroup consecutive records first (group 4i + lane/16 is one 16-lane row of
+// register i), then the group results in group order, again as one 16-lane tree.  The distributed
+// merge at the end of step_kernel takes the same two levels in separate workgroups, so every path
+// that merges a row's records produces the same bits.  Every lane ends with the result.
 __device__ __forceinline__ Stats merge_records(const float4 (&r)[kMaxVocabGroups / 64]) {
   constexpr int N = kMaxVocabGroups / 64;
-  float m = -INFINITY;
+  static_assert(N * 4 == kGroup, "the group results fit one 16-lane row");
+  Stats grp[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) m = fmaxf(m, r[i].x);
-  const float M = wave_max(m);
-  float s = 0.f;
-  int id = 0x7fffffff;
+  for (int i = 0; i < N; ++i) grp[i] = stats_row16_merge(stats_unpack(r[i]));
+  // lane j of every 16-lane row takes group j: register j/4 of any lane of row j%4
+  const int j = __lane_id() & 15;
+  const int src = 16 * (j & 3);
+  Stats mine = stats_empty();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    if (r[i].y != 0.f) s += r[i].y * ex2((r[i].x - M) * kLog2e);
-    if (r[i].x == M) id = min(id, __float_as_int(r[i].z));
+    Stats x;
+    x.m1 = __shfl(grp[i].m1, src);
+    x.s = __shfl(grp[i].s, src);
+    x.m2 = __shfl(grp[i].m2, src);
+    x.id = __shfl(grp[i].id, src);
+    if ((j >> 2) == i) mine = x;
   }
-  s = wave_sum(s);
-  id = wave_allreduce_min(id);
-  float sec = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < N; ++i) sec = fmaxf(sec, (r[i].x == M && __float_as_int(r[i].z) == id) ? r[i].w : r[i].x);
-  Stats t;
-  t.m1 = M;
-  t.s = s;
-  t.id = id;
-  t.m2 = wave_max(sec);
-  return t;
+  return stats_row16_merge(mine);
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -414,17 +421,23 @@ __device__ __forceinline__ uint64_t hierarchical_commit(uint64_t U, float conf, 
   return committed;
 }
 
-// State of one position of a sequence as the commit reads it (lane = position).
+// State of one position of a sequence as the commit reads it (lane = position), with the
+// sequence's rule and early-stop state: loading them here lets a caller prefetch all of it while
+// it waits for something else (the rule lookup is two dependent reads of the argument block).
 struct SeqState {
   bool masked;
   int st[DLM_CREDIT_SLOTS];
   float sc[DLM_CREDIT_SLOTS];
+  Rule rule;
+  int done;   // early-stop state on entry (DLM_SEQ_RUNNING without a state array)
 };
 
 __device__ __forceinline__ SeqState load_seq_state(const CommitArgs& a, int b) {
   const int l = __lane_id();
   const size_t row = (size_t)b * a.L + l;
   SeqState s;
+  s.rule = a.rules[a.rule_of[b]];
+  s.done = a.seq_done ? (int)a.seq_done[b] : DLM_SEQ_RUNNING;
   s.masked = l < a.L && a.mask[row] != 0;
 #pragma unroll
   for (int i = 0; i < DLM_CREDIT_SLOTS; ++i) {
@@ -447,12 +460,12 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
   const int l = __lane_id();
   const bool in = l < a.L;
   const size_t row = (size_t)b * a.L + l;
-  const Rule R = a.rules[a.rule_of[b]];
+  const Rule R = in_state.rule;
   if (!in) conf = -INFINITY;
 
   // early stop: a finished sequence only reports its candidates (its state stays as it is)
   const bool stopping = R.eos >= 0;
-  int done = stopping ? (int)a.seq_done[b] : DLM_SEQ_RUNNING;
+  int done = stopping ? in_state.done : DLM_SEQ_RUNNING;
   if (done == DLM_SEQ_FINISHED) {
     if (in) {
       if (a.out_tokens) a.out_tokens[row] = tok;
@@ -564,18 +577,40 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 }
 
 // ----------------------------------------------------------------------------------------------
-// Final merge + commit of sequences [b_begin, b_end): record g of row r sits at index
-// r*rs_row + g*rs_g of `rec` (rs_row = G, rs_g = 1 for the records of one head's workgroups;
-// rs_row = 1, rs_g = B*L for gathered vocabulary shards).  One wavefront per row (kRowBatch rows
-// with all their loads in flight together) merges the records in a fixed order; conf / token go
-// to LDS, then one wavefront per sequence commits.  With c.out_records the merged record itself
-// is written instead (ids offset by c.v_begin) and nothing commits.
+// Final merge + commit of sequences [b_begin, b_end).
+//   GROUPED = false: record g of row r sits at index r*rs_row + g*rs_g of `rec` (rs_row = G,
+//     rs_g = 1 for the records of one head's workgroups; rs_row = 1, rs_g = B*L for gathered
+//     vocabulary shards).  One wavefront per row (kRowBatch rows with all their loads in flight
+//     together) merges the G <= kMaxVocabGroups records with merge_records.
+//   GROUPED = true: `rec` holds the second-level records of the distributed merge, G <= kGroup per
+//     row at r*rs_row + g; one 16-lane row per row of the block (the second level of the same tree).
+// conf / token go to LDS, then one wavefront per sequence commits.  With c.out_records the merged
+// record itself is written instead (ids offset by c.v_begin) and nothing commits.
 // `pre` is the state this wavefront already fetched for sequence `pre_b` (or pre_b = -1).
 // Called by a whole workgroup; `smem` needs kRowsPerStage * 8 bytes.
 // ----------------------------------------------------------------------------------------------
+__device__ __forceinline__ void finalize_row(const CommitArgs& c, const Stats& t, int row, int rr, float* s_conf,
+                                             int* s_tok, bool do_commit) {
+  if (c.out_records) {
+    Stats o = t;
+    o.id = t.id + c.v_begin;
+    c.out_records[row] = stats_pack(o);
+    return;
+  }
+  // S >= 1 in exact arithmetic (the top logit's own term is 1); the exponent of that term
+  // carries the rounding of m*log2(e), so 1/S may land a few ulps above 1
+  const float conf = fminf(1.f / t.s, 1.f);
+  s_conf[rr] = conf;
+  s_tok[rr] = t.id;
+  if (c.out_conf) c.out_conf[row] = conf;
+  if (c.out_gap) c.out_gap[row] = t.m1 - t.m2;
+  if (!do_commit) c.out_tokens[row] = t.id;
+}
+
+template <bool GROUPED>
 __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t rec, int G, int rs_row, int rs_g,
                                    int b_begin, int b_end, uint4* smem, const SeqState& pre, int pre_b) {
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = lid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   float* s_conf = reinterpret_cast<float*>(smem);
@@ -584,39 +619,37 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
   for (int b0 = b_begin; b0 < b_end; b0 += seq_per_stage) {
     const int b1 = min(b_end, b0 + seq_per_stage);
     const int r_first = b0 * c.L, nrows = (b1 - b0) * c.L;
-    for (int rr0 = wave * kRowBatch; rr0 < nrows; rr0 += kWaves * kRowBatch) {
-      float4 buf[kRowBatch][kMaxVocabGroups / 64];
-#pragma unroll
-      for (int j = 0; j < kRowBatch; ++j) {
-        const int rr = rr0 + j;
-        const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
-#pragma unroll
-        for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
-          const int g = lane + 64 * i;
-          buf[j][i] = g < G ? record_load(rec, src + 16u * (unsigned)(g * rs_g)) : stats_pack(stats_empty());
-        }
+    if constexpr (GROUPED) {
+      for (int rr0 = wave * 4; rr0 < nrows; rr0 += kWaves * 4) {   // 4 rows per wavefront pass
+        const int rr = rr0 + (lane >> 4), j = lane & 15;
+        const bool rin = rr < nrows;
+        const unsigned src = (unsigned)((size_t)(r_first + (rin ? rr : 0)) * rs_row * 16);
+        float4 v = record_load(rec, j < G ? src + 16u * (unsigned)j : 0x80000000u);
+        v = j < G ? v : stats_pack(stats_empty());
+        const Stats t = stats_row16_merge(stats_unpack(v));
+        if (rin && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, do_commit);
       }
+    } else {
+      for (int rr0 = wave * kRowBatch; rr0 < nrows; rr0 += kWaves * kRowBatch) {
+        float4 buf[kRowBatch][kMaxVocabGroups / 64];
 #pragma unroll
-      for (int j = 0; j < kRowBatch; ++j) {
-        const int rr = rr0 + j;
-        float4 row_stats[kMaxVocabGroups / 64];
+        for (int j = 0; j < kRowBatch; ++j) {
+          const int rr = rr0 + j;
+          const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
 #pragma unroll
-        for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
-        const Stats t = merge_records(row_stats);
-        if (rr < nrows && lane == 0 && c.out_records) {
-          Stats o = t;
-          o.id = t.id + c.v_begin;
-          c.out_records[r_first + rr] = stats_pack(o);
-        } else if (rr < nrows && lane == 0) {
-          const int row = r_first + rr;
-          // S >= 1 in exact arithmetic (the top logit's own term is 1); the exponent of that
-          // term carries the rounding of m*log2(e), so 1/S may land a few ulps above 1
-          const float conf = fminf(1.f / t.s, 1.f);
-          s_conf[rr] = conf;
-          s_tok[rr] = t.id;
-          if (c.out_conf) c.out_conf[row] = conf;
-          if (c.out_gap) c.out_gap[row] = t.m1 - t.m2;
-          if (!do_commit) c.out_tokens[row] = t.id;
+          for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
+            const int g = lane + 64 * i;
+            buf[j][i] = g < G ? record_load(rec, src + 16u * (unsigned)(g * rs_g)) : stats_pack(stats_empty());
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < kRowBatch; ++j) {
+          const int rr = rr0 + j;
+          float4 row_stats[kMaxVocabGroups / 64];
+#pragma unroll
+          for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
+          const Stats t = merge_records(row_stats);
+          if (rr < nrows && lane == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, do_commit);
         }
       }
     }
@@ -667,10 +700,10 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   constexpr int LOGITS = kTileRows * MR;                 // logits of one tile
   constexpr int P = (LOGITS + kThreads - 1) / kThreads;  // logit slots per thread
   static_assert(RING % KFWM == 0, "ring must hold whole tiles");
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = lid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps the loop scalar
 
-  const int bid = blockIdx.x;
+  const int bid = gid();
   const int xcd = bid & 7, slot = bid >> 3;
   const int rg = slot % a.n_rg;
   const int gv = (slot / a.n_rg) * 8 + xcd;
@@ -836,15 +869,39 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   if constexpr (TK) return;   // finalize_topk_kernel follows on the stream
 
-  // ---- the last workgroup merges every row and commits ------------------------------------------
-  // Wrapping increment: the counter runs 0 .. gridDim.x-1 and the last arrival puts it back to 0,
-  // so a workspace that starts zeroed is zero again between calls.
+  // ---- two-level merge across workgroups --------------------------------------------------------
+  // The records of each group of kGroup consecutive vocabulary ranges are merged, row by row, by
+  // the group's last workgroup to finish; the last group to finish then merges the groups'
+  // records of every row and commits (the two levels of merge_records' tree).  Each counter is
+  // incremented with wrap-around: it runs 0 .. n-1 and its last arrival puts it back to 0, so a
+  // workspace that starts zeroed is zero again between calls.
   __shared__ int s_last;
+  const int grp = gv / kGroup;
+  const int gsize = min(kGroup, a.G_v - kGroup * grp);
+  if (tid == 0) {
+    const unsigned prev = __builtin_amdgcn_atomic_inc32(a.group_tickets + rg * a.nq + grp, (unsigned)(gsize - 1),
+                                                        __ATOMIC_RELAXED, "agent");
+    s_last = prev == (unsigned)(gsize - 1);
+  }
+  __syncthreads();
+  if (!s_last) return;
+  const __amdgpu_buffer_rsrc_t l2 = __builtin_amdgcn_make_buffer_rsrc(a.level2, 0, a.n_rg * MR * a.nq * 16, 0x00020000);
+  for (int rr = wave * 4 + (lane >> 4); rr < MR; rr += kWaves * 4) {   // 4 rows per wavefront pass
+    const int j = lane & 15, g = kGroup * grp + j;
+    const unsigned row = (unsigned)(rg * MR + rr);
+    float4 v = record_load(rec, g < a.G_v ? (row * (unsigned)a.G_v + (unsigned)g) * 16u : 0x80000000u);
+    v = g < a.G_v ? v : stats_pack(stats_empty());
+    const Stats t = stats_row16_merge(stats_unpack(v));
+    if (j == 0) record_store(l2, (row * (unsigned)a.nq + (unsigned)grp) * 16u, stats_pack(t));
+  }
+  __builtin_amdgcn_s_waitcnt(0);              // the group's records are out before it is counted
+  __syncthreads();
   const CommitArgs& c = a.c;
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   if (tid == 0) {
-    const unsigned prev = __builtin_amdgcn_atomic_inc32(a.ticket, gridDim.x - 1, __ATOMIC_RELAXED, "agent");
-    s_last = prev == gridDim.x - 1;
+    const unsigned total = (unsigned)(a.n_rg * a.nq);
+    const unsigned prev = __builtin_amdgcn_atomic_inc32(a.ticket, total - 1, __ATOMIC_RELAXED, "agent");
+    s_last = prev == total - 1;
   }
   // While the counter answers, each wavefront fetches the state of the sequence it would commit
   // first (only the last workgroup uses it; the others drop it).
@@ -853,7 +910,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  finalize_sequences(c, rec, a.G_v, a.G_v, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1);
+  finalize_sequences<true>(c, l2, a.nq, a.nq, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1);
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -928,11 +985,11 @@ struct GemmArgs {
 
 // Hidden rows -> MFMA fragment order: fragment (rb, kg) is 1 KB at (rb * H/16 + kg) * 1 KB, lane l
 // holding row 32rb + l%32, elements 16kg + 8(l/32) .. +8.  Rows past M are zero.
-__global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4* hp, int M, int H) {
+__global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4* hp, int M, int H, int nthreads) {
   const int KG = H / 16;
   const size_t n = (size_t)((M + 31) / 32) * KG * 64;
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+  const size_t stride = (size_t)nthreads;
+  for (size_t i = (size_t)gid() * 256 + lid(); i < n; i += stride) {
     const int l = (int)(i & 63);
     const size_t f = i >> 6;
     const int kg = (int)(f % KG), rb = (int)(f / KG);
@@ -1037,17 +1094,17 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
   __shared__ uint4 wring0[G::Slot], wring1[G::Slot], wring2[G::Slot], wring3[G::Slot];
   auto ring = [&](int slot) -> uint4* { return slot == 0 ? wring0 : slot == 1 ? wring1 : slot == 2 ? wring2 : wring3; };
   __shared__ float4 st_lds[kGemmWaves * G::HB * 64];  // running statistics, [wave][hb][lane]
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = lid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroups of one vocabulary range (one per row group) sit 8 block indices apart: one XCD
   int rg, gi;
   if ((a.G_t & 7) == 0) {
-    const int q = blockIdx.x >> 3;
+    const int q = gid() >> 3;
     rg = q % a.n_rg;
-    gi = (q / a.n_rg) * 8 + (blockIdx.x & 7);
+    gi = (q / a.n_rg) * 8 + (gid() & 7);
   } else {
-    rg = blockIdx.x % a.n_rg;
-    gi = blockIdx.x / a.n_rg;
+    rg = gid() % a.n_rg;
+    gi = gid() / a.n_rg;
   }
   rg = __builtin_amdgcn_readfirstlane(rg);                // (uniform; keeps the stage logic scalar)
   gi = __builtin_amdgcn_readfirstlane(gi);
@@ -1216,14 +1273,14 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_wide_tail_kernel(const Gemm
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, const float4* records, int G,
                                                             int nrows_total) {
   __shared__ uint4 stage[kRowsPerStage / 2];
-  const int b = blockIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = gid();
+  const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
   const __amdgpu_buffer_rsrc_t rec =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
   SeqState pre;
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   if (do_commit && wave == 0) pre = load_seq_state(c, b);
-  finalize_sequences(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  finalize_sequences<false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // Top-k export of one row (one wavefront).  Lane l holds the row's best-first lists g = l, l + 64,
@@ -1277,20 +1334,20 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
                                                                  int nrows_total) {
   constexpr int N = kMaxVocabGroups / 64;
   __shared__ uint4 stage[kRowsPerStage / 2];
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
   const __amdgpu_buffer_rsrc_t rec =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
-  if ((int)blockIdx.x < c.B) {
-    const int b = blockIdx.x;
+  if (gid() < c.B) {
+    const int b = gid();
     SeqState pre;
     const bool do_commit = (c.flags & kFlagCommit) != 0;
     if (do_commit && wave == 0) pre = load_seq_state(c, b);
-    finalize_sequences(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
+    finalize_sequences<false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
     return;
   }
-  const int row = ((int)blockIdx.x - c.B) * kWaves + wave;
+  const int row = (gid() - c.B) * kWaves + wave;
   if (row >= c.B * c.L) return;
-  const int lane = threadIdx.x & 63;
+  const int lane = lid() & 63;
   const __amdgpu_buffer_rsrc_t trec = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float4*>(topk_records), 0, nrows_total * G * (kTopK * 8), 0x00020000);
   constexpr unsigned kOOB = 0x80000000u;   // beyond any range: the load returns zeros
@@ -1325,33 +1382,33 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
 // the same merge and commit as the single-GPU head's, one workgroup per sequence.
 __global__ __launch_bounds__(kThreads) void merge_commit_kernel(const CommitArgs c, const float4* records, int G) {
   __shared__ uint4 stage[kRowsPerStage / 2];
-  const int b = blockIdx.x;
+  const int b = gid();
   const int M = c.B * c.L;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
   const __amdgpu_buffer_rsrc_t rec =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, G * M * 16, 0x00020000);
   SeqState pre;
   if (wave == 0) pre = load_seq_state(c, b);
-  finalize_sequences(c, rec, G, 1, M, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  finalize_sequences<false>(c, rec, G, 1, M, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // dlm_commit: conf / tokens given, one wavefront per sequence.
 __global__ __launch_bounds__(kThreads) void commit_kernel(const CommitArgs a, const float* conf, const int32_t* tok) {
-  const int b = blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int b = gid() * kWaves + (lid() >> 6);
   if (b >= a.B) return;
-  const int l = threadIdx.x & 63;
+  const int l = lid() & 63;
   const bool in = l < a.L;
   const size_t row = (size_t)b * a.L + l;
   commit_sequence(a, b, in ? conf[row] : 0.f, in ? tok[row] : 0, load_seq_state(a, b));
 }
 
 // dlm_workspace_init: zero fill.
-__global__ void fill_zero_kernel(uint8_t* p, size_t n) {
-  const size_t stride = (size_t)gridDim.x * blockDim.x;
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint8_t* p, size_t n, int nthreads) {
+  const size_t stride = (size_t)nthreads;
   const size_t nvec = n / 16;
   uint4* p4 = reinterpret_cast<uint4*>(p);
-  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nvec; i += stride) p4[i] = make_uint4(0, 0, 0, 0);
-  for (size_t i = nvec * 16 + (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) p[i] = 0;
+  for (size_t i = (size_t)gid() * 256 + lid(); i < nvec; i += stride) p4[i] = make_uint4(0, 0, 0, 0);
+  for (size_t i = nvec * 16 + (size_t)gid() * 256 + lid(); i < n; i += stride) p[i] = 0;
 }
 
 }  // namespace dlm

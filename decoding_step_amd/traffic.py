@@ -8,8 +8,8 @@ the summaries under ``profiles/``, tagged with a hash of the kernel sources and 
 flags; ``bench.py`` reports it as ``roofline.traffic`` only while that hash matches.
 
     python -m decoding_step_amd.traffic --workload mixed_b16_l32 --kernel gemm_wide_kernel \\
-        --fetch gpurun_out/pmc_FETCH --write gpurun_out/pmc_WRITE \\
-        --copy-fetch gpurun_out/pmc_copy_FETCH --copy-write gpurun_out/pmc_copy_WRITE
+        --fetch prof/pmc_FETCH --write prof/pmc_WRITE \\
+        --copy-fetch prof/pmc_copy_FETCH --copy-write prof/pmc_copy_WRITE
 """
 from __future__ import annotations
 

@@ -55,11 +55,13 @@ def test_header_constants_match_binding():
 
 
 def test_workspace_sizes():
-    # counter line (256 B) + one 16-byte record per (padded row, vocabulary range); rows are
-    # padded to 16, 32 or 64 per row group and there are at most 256 vocabulary ranges
-    assert nat.dlm_workspace_bytes(1, 32, 2048, 126464, nat.DLM_BF16) == 256 + 32 * 256 * 16
-    assert nat.dlm_workspace_bytes(1, 64, 2048, 126464, nat.DLM_BF16) == 256 + 64 * 256 * 16
-    assert nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_F32) == 256 + 16 * 64 * 16      # 64 tiles
+    # streaming plan: counters (one global + one per group of 16 vocabulary ranges, padded to
+    # 256 B) + one 16-byte record per (padded row, vocabulary range) + one second-level record
+    # per (padded row, group); rows are padded to 16, 32 or 64 per row group and there are at most
+    # 256 vocabulary ranges (16 groups)
+    assert nat.dlm_workspace_bytes(1, 32, 2048, 126464, nat.DLM_BF16) == 256 + 32 * 256 * 16 + 32 * 16 * 16
+    assert nat.dlm_workspace_bytes(1, 64, 2048, 126464, nat.DLM_BF16) == 256 + 64 * 256 * 16 + 64 * 16 * 16
+    assert nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_F32) == 256 + 16 * 64 * 16 + 16 * 4 * 16  # 64 tiles
     # GEMM-shaped path (bf16, more than 64 rows): records for every (padded row, workgroup of its
     # row group), then the hidden rows in fragment order (rows padded to 32); 256-row groups,
     # 256-row vocabulary tiles, workgroups per group a multiple of 8 where there are enough tiles
@@ -196,10 +198,13 @@ def test_decode_steps_validation():
 def test_topk_workspace_sizes():
     # top-k on: the streaming plan for every shape, plus one list of 8 (logit, id) pairs (64 bytes)
     # per (padded row, vocabulary range) after the statistics records
-    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 8) == 256 + 32 * 256 * 16 + 32 * 256 * 64
-    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 3) == 256 + 32 * 256 * 16 + 32 * 256 * 64
-    # 512 bf16 rows: 64-row groups (8 of them), 32 vocabulary ranges each, no packed hidden rows
-    assert nat.dlm_workspace_bytes_topk(16, 32, 2048, 157184, nat.DLM_BF16, 8) == 256 + 512 * 32 * 16 + 512 * 32 * 64
+    base = 256 + 32 * 256 * 16 + 32 * 16 * 16
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 8) == base + 32 * 256 * 64
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 3) == base + 32 * 256 * 64
+    # 512 bf16 rows: 64-row groups (8 of them), 32 vocabulary ranges (2 groups) each, no packed
+    # hidden rows
+    assert nat.dlm_workspace_bytes_topk(16, 32, 2048, 157184, nat.DLM_BF16, 8) == \
+        256 + 512 * 32 * 16 + 512 * 2 * 16 + 512 * 32 * 64
     for B, L, H, V, dt in [(1, 32, 2048, 126464, 1), (16, 32, 2048, 157184, 1), (1, 8, 64, 1024, 0)]:
         assert nat.dlm_workspace_bytes_topk(B, L, H, V, dt, 0) == nat.dlm_workspace_bytes(B, L, H, V, dt)
     assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 9) == 0
