@@ -63,8 +63,8 @@ struct CommitArgs {
 // LDS of the step kernel for NMB 16-row blocks: two buffers of per-wavefront partial logits
 // (8 waves x NMB x 1 KB each), reused for the per-slot statistics and the finalize stage.
 __host__ __device__ constexpr size_t lds_bytes(int NMB) {
-  return (size_t)2 * kWaves * NMB * 1024 > (size_t)kRowsPerStage * 8 ? (size_t)2 * kWaves * NMB * 1024
-                                                                      : (size_t)kRowsPerStage * 8;
+  return (size_t)2 * kWaves * NMB * 1024 > (size_t)kRowsPerStage * 12 ? (size_t)2 * kWaves * NMB * 1024
+                                                                       : (size_t)kRowsPerStage * 12;
 }
 
 // With the top-k fold the per-slot statistics (16 bytes) are followed by the per-slot lists
@@ -460,12 +460,19 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
   const int l = __lane_id();
   const bool in = l < a.L;
   const size_t row = (size_t)b * a.L + l;
-  const Rule R = in_state.rule;
+  // the rule and the early-stop state are the same in every lane: scalar registers, so the
+  // policy branches are uniform jumps
+  Rule R;
+  R.kind = __builtin_amdgcn_readfirstlane(in_state.rule.kind);
+  R.thr = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, in_state.rule.thr)));
+  R.decay = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, in_state.rule.decay)));
+  R.depth = __builtin_amdgcn_readfirstlane(in_state.rule.depth);
+  R.eos = __builtin_amdgcn_readfirstlane(in_state.rule.eos);
   if (!in) conf = -INFINITY;
 
   // early stop: a finished sequence only reports its candidates (its state stays as it is)
   const bool stopping = R.eos >= 0;
-  int done = stopping ? in_state.done : DLM_SEQ_RUNNING;
+  int done = stopping ? __builtin_amdgcn_readfirstlane(in_state.done) : DLM_SEQ_RUNNING;
   if (done == DLM_SEQ_FINISHED) {
     if (in) {
       if (a.out_tokens) a.out_tokens[row] = tok;
@@ -587,10 +594,13 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 // conf / token go to LDS, then one wavefront per sequence commits.  With c.out_records the merged
 // record itself is written instead (ids offset by c.v_begin) and nothing commits.
 // `pre` is the state this wavefront already fetched for sequence `pre_b` (or pre_b = -1).
-// Called by a whole workgroup; `smem` needs kRowsPerStage * 8 bytes.
+// The per-row outputs (confidence, gap, and the candidates without a commit) are written after the
+// commits: a wavefront's vector-memory counter also counts its stores, so a store issued before a
+// commit would make the commit's wait for its loaded state wait for the store's acknowledgement.
+// Called by a whole workgroup; `smem` needs kRowsPerStage * 12 bytes.
 // ----------------------------------------------------------------------------------------------
 __device__ __forceinline__ void finalize_row(const CommitArgs& c, const Stats& t, int row, int rr, float* s_conf,
-                                             int* s_tok, bool do_commit) {
+                                             int* s_tok, float* s_gap) {
   if (c.out_records) {
     Stats o = t;
     o.id = t.id + c.v_begin;
@@ -599,12 +609,9 @@ __device__ __forceinline__ void finalize_row(const CommitArgs& c, const Stats& t
   }
   // S >= 1 in exact arithmetic (the top logit's own term is 1); the exponent of that term
   // carries the rounding of m*log2(e), so 1/S may land a few ulps above 1
-  const float conf = fminf(1.f / t.s, 1.f);
-  s_conf[rr] = conf;
+  s_conf[rr] = fminf(1.f / t.s, 1.f);
   s_tok[rr] = t.id;
-  if (c.out_conf) c.out_conf[row] = conf;
-  if (c.out_gap) c.out_gap[row] = t.m1 - t.m2;
-  if (!do_commit) c.out_tokens[row] = t.id;
+  s_gap[rr] = t.m1 - t.m2;
 }
 
 template <bool GROUPED>
@@ -615,6 +622,7 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   float* s_conf = reinterpret_cast<float*>(smem);
   int* s_tok = reinterpret_cast<int*>(smem) + kRowsPerStage;
+  float* s_gap = reinterpret_cast<float*>(smem) + 2 * kRowsPerStage;
   const int seq_per_stage = max(1, kRowsPerStage / c.L);
   for (int b0 = b_begin; b0 < b_end; b0 += seq_per_stage) {
     const int b1 = min(b_end, b0 + seq_per_stage);
@@ -627,7 +635,7 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
         float4 v = record_load(rec, j < G ? src + 16u * (unsigned)j : 0x80000000u);
         v = j < G ? v : stats_pack(stats_empty());
         const Stats t = stats_row16_merge(stats_unpack(v));
-        if (rin && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, do_commit);
+        if (rin && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
       }
     } else {
       for (int rr0 = wave * kRowBatch; rr0 < nrows; rr0 += kWaves * kRowBatch) {
@@ -649,7 +657,7 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
 #pragma unroll
           for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
           const Stats t = merge_records(row_stats);
-          if (rr < nrows && lane == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, do_commit);
+          if (rr < nrows && lane == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
         }
       }
     }
@@ -660,6 +668,14 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
         const bool in = lane < c.L;
         const SeqState sq = b == pre_b ? pre : load_seq_state(c, b);
         commit_sequence(c, b, in ? s_conf[off] : 0.f, in ? s_tok[off] : 0, sq);
+      }
+    }
+    if (!c.out_records) {
+      for (int rr = tid; rr < nrows; rr += kThreads) {
+        const int row = r_first + rr;
+        if (c.out_conf) c.out_conf[row] = s_conf[rr];
+        if (c.out_gap) c.out_gap[row] = s_gap[rr];
+        if (!do_commit) c.out_tokens[row] = s_tok[rr];
       }
     }
     __syncthreads();
@@ -1272,7 +1288,7 @@ __global__ __launch_bounds__(kGemmThreads) void gemm_wide_tail_kernel(const Gemm
 // Merge + commit after the GEMM-path kernel: one workgroup per sequence.
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, const float4* records, int G,
                                                             int nrows_total) {
-  __shared__ uint4 stage[kRowsPerStage / 2];
+  __shared__ uint4 stage[kRowsPerStage * 12 / 16];
   const int b = gid();
   const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
   const __amdgpu_buffer_rsrc_t rec =
@@ -1333,7 +1349,7 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
                                                                  const float4* topk_records, int G,
                                                                  int nrows_total) {
   constexpr int N = kMaxVocabGroups / 64;
-  __shared__ uint4 stage[kRowsPerStage / 2];
+  __shared__ uint4 stage[kRowsPerStage * 12 / 16];
   const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
   const __amdgpu_buffer_rsrc_t rec =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
@@ -1381,7 +1397,7 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
 // Merge + commit of gathered vocabulary shards (records [G][B*L], shards in vocabulary order):
 // the same merge and commit as the single-GPU head's, one workgroup per sequence.
 __global__ __launch_bounds__(kThreads) void merge_commit_kernel(const CommitArgs c, const float4* records, int G) {
-  __shared__ uint4 stage[kRowsPerStage / 2];
+  __shared__ uint4 stage[kRowsPerStage * 12 / 16];
   const int b = gid();
   const int M = c.B * c.L;
   const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
