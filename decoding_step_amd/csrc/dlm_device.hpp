@@ -316,18 +316,33 @@ __device__ __forceinline__ void stats_fold1(Stats& st, float z, int v) {
 // register i), then the group results in group order, again as one 16-lane tree.  The distributed
 // merge at the end of step_kernel takes the same two levels in separate workgroups, so every path
 // that merges a row's records produces the same bits.  Every lane ends with the result.
-__device__ __forceinline__ Stats merge_records(const float4 (&r)[kMaxVocabGroups / 64]) {
+// G: records present (r[i] past G hold empty records).  Merging with an empty record gives the
+// other operand exactly (its maximum, sum, id and runner-up unchanged), so slices and groups past G
+// are skipped and a single group is the result as it stands: the same bits, less work.
+__device__ __forceinline__ Stats merge_records(const float4 (&r)[kMaxVocabGroups / 64], int G) {
   constexpr int N = kMaxVocabGroups / 64;
   static_assert(N * 4 == kGroup, "the group results fit one 16-lane row");
   Stats grp[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) grp[i] = stats_row16_merge(stats_unpack(r[i]));
+  for (int i = 0; i < N; ++i) {
+    if (64 * i < G) grp[i] = stats_row16_merge(stats_unpack(r[i]));   // uniform branch
+    else grp[i] = stats_empty();
+  }
+  if (G <= kGroup) {                      // one group: lane 0's row holds the result
+    Stats t;
+    t.m1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, grp[0].m1)));
+    t.s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, grp[0].s)));
+    t.m2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, grp[0].m2)));
+    t.id = __builtin_amdgcn_readfirstlane(grp[0].id);
+    return t;
+  }
   // lane j of every 16-lane row takes group j: register j/4 of any lane of row j%4
   const int j = __lane_id() & 15;
   const int src = 16 * (j & 3);
   Stats mine = stats_empty();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
+    if (64 * i >= G) break;                 // uniform: the remaining groups are empty
     Stats x;
     x.m1 = __shfl(grp[i].m1, src);
     x.s = __shfl(grp[i].s, src);
@@ -656,7 +671,7 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
           float4 row_stats[kMaxVocabGroups / 64];
 #pragma unroll
           for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
-          const Stats t = merge_records(row_stats);
+          const Stats t = merge_records(row_stats, G);
           if (rr < nrows && lane == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
         }
       }
@@ -1390,7 +1405,7 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
       t[n].id[2 * j + 1] = in ? __float_as_int(e[n][j].w) : kNoToken;
     }
   }
-  const Stats st = merge_records(r);
+  const Stats st = merge_records(r, G);
   topk_merge_row<N>(c, t, row, st.m1, 1.f / st.s);
 }
 
