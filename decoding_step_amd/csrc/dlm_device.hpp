@@ -704,9 +704,10 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
 // wavefronts each.  Workgroup ids are dealt round-robin over the 8 XCDs; the row groups of one
 // vocabulary range sit on the same XCD back to back, so repeated W reads of a range hit its L2.
 //
-// Streaming: the 8 wavefronts share every 16-row vocabulary tile.  Wavefront w owns the K
-// fragments w, w+8, w+16, ... of each row (so together they sweep each row left to right) and
-// keeps the matching hidden-state fragments in registers for the whole kernel.  W fragments go
+// Streaming: the 8 wavefronts share every 16-row vocabulary tile.  Wavefront w owns the 64-byte K
+// fragment pairs (2w, 2w+1), (16+2w, 16+2w+1), ... of each row (whole 128-byte lines; together
+// the wavefronts sweep each row left to right) and keeps the matching hidden-state fragments in
+// registers for the whole kernel.  W fragments go
 // straight from HBM into a ring of registers (RING loads in flight per lane) and through the
 // matrix cores.  At the end of a tile each wavefront leaves its partial logits in LDS; after one
 // barrier every thread sums the 8 partials of its (row, vocabulary slot) and folds the logit into
@@ -759,9 +760,15 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<char*>(static_cast<const char*>(a.W) + row0 * row_bytes), 0, (int)nbytes, 0x00020000);
 
-  // byte offset of fragment kf = j*8 + wave of tile t (zero-filled past the range or the row)
+  // K fragment j of this wavefront: the wavefronts take adjacent pairs of 64-byte fragments,
+  // (2w, 2w+1), (16+2w, 16+2w+1), ..., so fragments j and j+1 (j even) are the two halves of the
+  // same 128-byte lines and every line a wavefront touches is used whole.  KFWM is even.
+  static_assert(KFWM % 2 == 0, "fragments go in pairs");
+  auto frag = [&](int j) -> int { return (j >> 1) * (2 * kWaves) + 2 * wave + (j & 1); };
+
+  // byte offset of fragment j of tile t (zero-filled past the range or the row)
   auto w_off = [&](int t, int j) -> unsigned {
-    const int kf = j * kWaves + wave;
+    const int kf = frag(j);
     return (t < nloc && kf < F) ? (unsigned)t * kTileRows * row_bytes + lane_off + (unsigned)kf * 64u : kOOB;
   };
 
@@ -778,7 +785,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
         const_cast<void*>(a.hidden), 0, a.M * (int)row_bytes, 0x00020000);
 #pragma unroll
     for (int j = 0; j < KFWM; ++j) {
-      const int kf = j * kWaves + wave;
+      const int kf = frag(j);
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
         const unsigned row = (unsigned)(rg * MR + mb * 16 + (lane & 15));
@@ -810,42 +817,48 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  auto mma_frag = [&](const uint4& w, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) acc[mb] = E::mma(w, hreg[j][mb], acc[mb]);
+  };
+  // tile r done: partials to LDS, one barrier, every thread folds its logit slots
+  auto tile_end = [&](int r) __attribute__((always_inline)) {
+    float* buf = red + (r & 1) * (kWaves * NMB * 256);
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb) {
+      *reinterpret_cast<f32x4*>(buf + ((wave * NMB + mb) * 64 + lane) * 4) = acc[mb];
+      acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    __syncthreads();
+    if (r < nloc) {
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const int f = tid + p * kThreads;          // slot: (mb, lane, component) of the tile
+        if (f < LOGITS) {
+          const int mb = f >> 8, rest = f & 255;
+          float z = 0.f;
+#pragma unroll
+          for (int w = 0; w < kWaves; ++w) z += buf[(w * NMB + mb) * 256 + rest];
+          const int v = (t_begin + r) * kTileRows + 4 * (rest >> 6) + (rest & 3);
+          if (v < a.V) {
+            stats_fold1(st[p], z, v);
+            if constexpr (TK) topk_push_ascending(tk[p], z, v);
+          }
+        }
+      }
+    }
+  };
+
   for (int r0 = 0; r0 < nloc_p; r0 += G) {
 #pragma unroll
     for (int u = 0; u < G; ++u) {
 #pragma unroll
       for (int j = 0; j < KFWM; ++j) {
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) acc[mb] = E::mma(ring[u * KFWM + j], hreg[j][mb], acc[mb]);
+        mma_frag(ring[u * KFWM + j], j);
         ring[u * KFWM + j] = buffer_load16(wrs, w_off(r0 + u + G, j));
         __builtin_amdgcn_sched_barrier(0);  // keep consume-then-refill order: the wait stays RING-1 deep
       }
-      // tile r done: partials to LDS, one barrier, every thread folds its logit slots
-      const int r = r0 + u;
-      float* buf = red + (r & 1) * (kWaves * NMB * 256);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        *reinterpret_cast<f32x4*>(buf + ((wave * NMB + mb) * 64 + lane) * 4) = acc[mb];
-        acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      __syncthreads();
-      if (r < nloc) {
-#pragma unroll
-        for (int p = 0; p < P; ++p) {
-          const int f = tid + p * kThreads;          // slot: (mb, lane, component) of the tile
-          if (f < LOGITS) {
-            const int mb = f >> 8, rest = f & 255;
-            float z = 0.f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) z += buf[(w * NMB + mb) * 256 + rest];
-            const int v = (t_begin + r) * kTileRows + 4 * (rest >> 6) + (rest & 3);
-            if (v < a.V) {
-              stats_fold1(st[p], z, v);
-              if constexpr (TK) topk_push_ascending(tk[p], z, v);
-            }
-          }
-        }
-      }
+      tile_end(r0 + u);
     }
   }
 
