@@ -22,7 +22,6 @@ constexpr int kThreads = kWaves * 64; // workgroup size
 constexpr int kTileRows = 16;         // vocabulary rows per MFMA tile
 constexpr int kPrefetch = 8;          // 16-byte W fragments in flight per lane (measured: 8 beats 16 and 32)
 constexpr int kRowsPerStage = 1024;   // finalize: rows staged in LDS at a time
-constexpr int kRowBatch = 4;          // finalize: rows per wavefront with loads in flight together
 constexpr int kMaxVocabGroups = 256;  // vocabulary ranges (records per row) at most
 constexpr int kGroup = 16;            // records per first-level group of the cross-workgroup merge
 constexpr unsigned kFlagCommit = 1u << 16;  // internal: run the commit policies
@@ -173,15 +172,32 @@ __device__ __forceinline__ Stats stats_empty() {
   return t;
 }
 
+// Symmetric in its operands, bit for bit (every operation in it is), and an empty operand leaves
+// the other unchanged: any grouping of records that follows the same tree gives the same bits.
+// The larger maximum's sum is rescaled by exp(0) = 1 exactly, so only the other sum needs an
+// exponential (the sum of zero stays zero, also for two empty operands).
 __device__ __forceinline__ Stats stats_merge(const Stats& a, const Stats& b) {
   Stats r;
   r.m1 = fmaxf(a.m1, b.m1);
-  const float sa = a.s == 0.f ? 0.f : a.s * ex2((a.m1 - r.m1) * kLog2e);
-  const float sb = b.s == 0.f ? 0.f : b.s * ex2((b.m1 - r.m1) * kLog2e);
-  r.s = sa + sb;
+  const float lo = fminf(a.m1, b.m1);
+  const bool a_hi = a.m1 >= b.m1;
+  const float s_hi = a_hi ? a.s : b.s, s_lo = a_hi ? b.s : a.s;
+  r.s = s_hi + (s_lo == 0.f ? 0.f : s_lo * ex2((lo - r.m1) * kLog2e));
   r.id = a.m1 > b.m1 ? a.id : (b.m1 > a.m1 ? b.id : min(a.id, b.id));
-  r.m2 = fmaxf(fmaxf(a.m2, b.m2), fminf(a.m1, b.m1));
+  r.m2 = fmaxf(fmaxf(a.m2, b.m2), lo);
   return r;
+}
+
+// Balanced binary tree over v[0..N) in index order, ((v0 v1)(v2 v3))((v4 v5)(v6 v7))..., held in
+// one lane's registers: the tree stats_row16_merge builds across the 16 lanes of a row.
+template <int N>
+__device__ __forceinline__ Stats stats_tree(Stats (&v)[N]) {
+  static_assert((N & (N - 1)) == 0, "a power of two");
+#pragma unroll
+  for (int w = 1; w < N; w *= 2)
+#pragma unroll
+    for (int i = 0; i < N; i += 2 * w) v[i] = stats_merge(v[i], v[i + w]);
+  return v[0];
 }
 
 template <int CTRL>
@@ -201,6 +217,27 @@ __device__ __forceinline__ Stats stats_row16_merge(Stats t) {
   t = stats_merge(t, stats_dpp<kDppHalfMirror>(t));
   t = stats_merge(t, stats_dpp<kDppMirror>(t));
   return t;
+}
+
+// Every lane gets the merge of its value with the same lane's value in the row W lanes away
+// (W = 16: rows 0+1 and 2+3; W = 32: rows 0+2 and 1+3).
+template <int W>
+__device__ __forceinline__ Stats stats_merge_rows(const Stats& t) {
+  Stats a, b;
+  int lo, hi;
+  row_swap<W>(__builtin_bit_cast(int, t.m1), lo, hi);
+  a.m1 = __builtin_bit_cast(float, lo);
+  b.m1 = __builtin_bit_cast(float, hi);
+  row_swap<W>(__builtin_bit_cast(int, t.s), lo, hi);
+  a.s = __builtin_bit_cast(float, lo);
+  b.s = __builtin_bit_cast(float, hi);
+  row_swap<W>(__builtin_bit_cast(int, t.m2), lo, hi);
+  a.m2 = __builtin_bit_cast(float, lo);
+  b.m2 = __builtin_bit_cast(float, hi);
+  row_swap<W>(t.id, lo, hi);
+  a.id = lo;
+  b.id = hi;
+  return stats_merge(a, b);
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -311,46 +348,35 @@ __device__ __forceinline__ void stats_fold1(Stats& st, float z, int v) {
   st.m1 = mnew;
 }
 
-// Merge the records of one row held by a wavefront (record g = lane + 64*i) in a fixed two-level
-// tree: the groups of kGroup consecutive records first (group 4i + lane/16 is one 16-lane row of
-// register i), then the group results in group order, again as one 16-lane tree.  The distributed
-// merge at the end of step_kernel takes the same two levels in separate workgroups, so every path
-// that merges a row's records produces the same bits.  Every lane ends with the result.
-// G: records present (r[i] past G hold empty records).  Merging with an empty record gives the
-// other operand exactly (its maximum, sum, id and runner-up unchanged), so slices and groups past G
-// are skipped and a single group is the result as it stands: the same bits, less work.
-__device__ __forceinline__ Stats merge_records(const float4 (&r)[kMaxVocabGroups / 64], int G) {
-  constexpr int N = kMaxVocabGroups / 64;
-  static_assert(N * 4 == kGroup, "the group results fit one 16-lane row");
-  Stats grp[N];
+// Merge the records of one row in a fixed two-level tree: the groups of kGroup consecutive
+// records first (a balanced binary tree over each group, in index order), then the group results,
+// in group order, as one more such tree.  The distributed merge at the end of step_kernel takes
+// the same two levels in separate workgroups (16-lane DPP trees), so every path that merges a
+// row's records produces the same bits.  Merging with an empty record gives the other operand
+// exactly, so records past G are empty ones and skipped work changes no bits.
+//
+// merge_records: one row per wavefront, lane l holding records 16*(l%16) + 4*(l/16) + i (i < 4):
+// the quarter of group l%16 in registers, the four quarters across rows (row swaps), the groups
+// across the 16 lanes of a row.  Every lane ends with the result.
+constexpr int kRecordsPerLane = kMaxVocabGroups / 64;
+static_assert(kRecordsPerLane == 4 && kGroup == 16, "a group is four quarters of four records");
+__device__ __forceinline__ int record_of_lane(int lane, int i) { return 16 * (lane & 15) + 4 * (lane >> 4) + i; }
+
+__device__ __forceinline__ Stats merge_records(const float4 (&r)[kRecordsPerLane], int G) {
+  Stats q[kRecordsPerLane];
 #pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (64 * i < G) grp[i] = stats_row16_merge(stats_unpack(r[i]));   // uniform branch
-    else grp[i] = stats_empty();
-  }
-  if (G <= kGroup) {                      // one group: lane 0's row holds the result
-    Stats t;
-    t.m1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, grp[0].m1)));
-    t.s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, grp[0].s)));
-    t.m2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, grp[0].m2)));
-    t.id = __builtin_amdgcn_readfirstlane(grp[0].id);
-    return t;
-  }
-  // lane j of every 16-lane row takes group j: register j/4 of any lane of row j%4
-  const int j = __lane_id() & 15;
-  const int src = 16 * (j & 3);
-  Stats mine = stats_empty();
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    if (64 * i >= G) break;                 // uniform: the remaining groups are empty
-    Stats x;
-    x.m1 = __shfl(grp[i].m1, src);
-    x.s = __shfl(grp[i].s, src);
-    x.m2 = __shfl(grp[i].m2, src);
-    x.id = __shfl(grp[i].id, src);
-    if ((j >> 2) == i) mine = x;
-  }
-  return stats_row16_merge(mine);
+  for (int i = 0; i < kRecordsPerLane; ++i) q[i] = stats_unpack(r[i]);
+  Stats t = stats_tree(q);
+  t = stats_merge_rows<16>(t);
+  t = stats_merge_rows<32>(t);            // group l%16 in every lane of column l%16
+  if (G > kGroup) return stats_row16_merge(t);
+  // one group (uniform branch): it is the result as it stands, in lane 0
+  Stats b;
+  b.m1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.m1)));
+  b.s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.s)));
+  b.m2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.m2)));
+  b.id = __builtin_amdgcn_readfirstlane(t.id);
+  return b;
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -602,8 +628,9 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 // Final merge + commit of sequences [b_begin, b_end).
 //   GROUPED = false: record g of row r sits at index r*rs_row + g*rs_g of `rec` (rs_row = G,
 //     rs_g = 1 for the records of one head's workgroups; rs_row = 1, rs_g = B*L for gathered
-//     vocabulary shards).  One wavefront per row (kRowBatch rows with all their loads in flight
-//     together) merges the G <= kMaxVocabGroups records with merge_records.
+//     vocabulary shards), G <= kMaxVocabGroups.  One 16-lane row per row of the block: lane j
+//     loads group j's records and merges them in registers, then the 16 lanes merge the groups
+//     (merge_records' tree, four rows per wavefront at once).
 //   GROUPED = true: `rec` holds the second-level records of the distributed merge, G <= kGroup per
 //     row at r*rs_row + g; one 16-lane row per row of the block (the second level of the same tree).
 // conf / token go to LDS, then one wavefront per sequence commits.  With c.out_records the merged
@@ -642,39 +669,31 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
   for (int b0 = b_begin; b0 < b_end; b0 += seq_per_stage) {
     const int b1 = min(b_end, b0 + seq_per_stage);
     const int r_first = b0 * c.L, nrows = (b1 - b0) * c.L;
-    if constexpr (GROUPED) {
-      for (int rr0 = wave * 4; rr0 < nrows; rr0 += kWaves * 4) {   // 4 rows per wavefront pass
-        const int rr = rr0 + (lane >> 4), j = lane & 15;
-        const bool rin = rr < nrows;
-        const unsigned src = (unsigned)((size_t)(r_first + (rin ? rr : 0)) * rs_row * 16);
-        float4 v = record_load(rec, j < G ? src + 16u * (unsigned)j : 0x80000000u);
+    // 4 rows per wavefront pass, one per 16-lane row; lane j of a row takes group j
+    for (int rr0 = wave * 4; rr0 < nrows; rr0 += kWaves * 4) {
+      const int rr = rr0 + (lane >> 4), j = lane & 15;
+      const bool rin = rr < nrows;
+      const unsigned src = (unsigned)((size_t)(r_first + (rin ? rr : 0)) * rs_row * 16);
+      Stats t;
+      if (GROUPED || G <= kGroup) {
+        // at most one group: record j in lane j, one 16-lane tree
+        float4 v = record_load(rec, j < G ? src + 16u * (unsigned)(j * rs_g) : 0x80000000u);
         v = j < G ? v : stats_pack(stats_empty());
-        const Stats t = stats_row16_merge(stats_unpack(v));
-        if (rin && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
-      }
-    } else {
-      for (int rr0 = wave * kRowBatch; rr0 < nrows; rr0 += kWaves * kRowBatch) {
-        float4 buf[kRowBatch][kMaxVocabGroups / 64];
+        t = stats_row16_merge(stats_unpack(v));
+      } else {
+        // group j's records in lane j's registers (its tree in registers), then the groups
+        float4 v[kGroup];
 #pragma unroll
-        for (int j = 0; j < kRowBatch; ++j) {
-          const int rr = rr0 + j;
-          const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
-#pragma unroll
-          for (int i = 0; i < kMaxVocabGroups / 64; ++i) {
-            const int g = lane + 64 * i;
-            buf[j][i] = g < G ? record_load(rec, src + 16u * (unsigned)(g * rs_g)) : stats_pack(stats_empty());
-          }
+        for (int k = 0; k < kGroup; ++k) {
+          const int g = kGroup * j + k;
+          v[k] = record_load(rec, g < G ? src + 16u * (unsigned)(g * rs_g) : 0x80000000u);
         }
+        Stats q[kGroup];
 #pragma unroll
-        for (int j = 0; j < kRowBatch; ++j) {
-          const int rr = rr0 + j;
-          float4 row_stats[kMaxVocabGroups / 64];
-#pragma unroll
-          for (int i = 0; i < kMaxVocabGroups / 64; ++i) row_stats[i] = buf[j][i];
-          const Stats t = merge_records(row_stats, G);
-          if (rr < nrows && lane == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
-        }
+        for (int k = 0; k < kGroup; ++k) q[k] = kGroup * j + k < G ? stats_unpack(v[k]) : stats_empty();
+        t = stats_row16_merge(stats_tree(q));
       }
+      if (rin && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
     }
     __syncthreads();
     if (do_commit) {
@@ -1399,8 +1418,9 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
   float4 e[N][kTopK / 2];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    const int g = lane + 64 * n;
-    r[n] = record_load(rec, g < G ? (unsigned)(((size_t)row * G + g) * 16) : kOOB);
+    const int gs = record_of_lane(lane, n);   // statistics: merge_records' layout
+    r[n] = record_load(rec, gs < G ? (unsigned)(((size_t)row * G + gs) * 16) : kOOB);
+    const int g = lane + 64 * n;              // lists: any layout (they merge by value)
 #pragma unroll
     for (int j = 0; j < kTopK / 2; ++j)
       e[n][j] = record_load(trec, g < G ? (unsigned)(((size_t)row * G + g) * (kTopK * 8) + 16 * j) : kOOB);
@@ -1409,7 +1429,7 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     const bool in = lane + 64 * n < G;
-    r[n] = in ? r[n] : stats_pack(stats_empty());
+    r[n] = record_of_lane(lane, n) < G ? r[n] : stats_pack(stats_empty());
 #pragma unroll
     for (int j = 0; j < kTopK / 2; ++j) {
       t[n].z[2 * j] = in ? e[n][j].x : -INFINITY;
