@@ -792,28 +792,57 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   };
 
   // ---- hidden fragments of this wavefront's K positions, in registers ------------------------
-  // rows past M and fragments past F read as zero (outside the buffer range).  Hidden fragment j
-  // goes out just before W fragment j of the first tile: loads retire in issue order, so the
-  // first tile's MFMAs on fragment j wait for fragments 0..j only, and the rest of the hidden
-  // rows arrive while the W stream is already running.
+  // Every workgroup reads all hidden rows before its first tile completes, so their loads use
+  // whole 128-byte lines: for the fragment pair (2q, 2q+1) of a 16-row block, lane l loads chunk
+  // l%8 of the pair's 128 bytes of row l/8 (rows 0-7), then of row 8 + l/8.  The two loads go
+  // through this wavefront's 2 KB of LDS per block (chunk c of row r at slot c ^ ((r/2)%8): 16
+  // lanes hit 16 distinct 16-byte bank groups) and come back in the MFMA layout: row l%16, chunk
+  // l/16 of fragment 2q or 2q+1.  (Loads of the MFMA layout itself cover 16 half lines each and
+  // arrived at about two thirds of the rate.)  Rows past M and fragments past F read as zero.
+  // Hidden pair q goes out just before W fragments 2q, 2q+1 of the first tile.
   uint4 hreg[KFWM][NMB];
   // ring slot u*KFWM + j always holds fragment j of a tile congruent to u modulo G
   uint4 ring[RING];
   {
     const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(a.hidden), 0, a.M * (int)row_bytes, 0x00020000);
+    constexpr int NQ = KFWM / 2;
+    uint4 hl[NQ][NMB][2];                                  // [pair][block][rows 0-7 | rows 8-15]
+    const int c_ld = lane & 7, r_ld = lane >> 3;           // loading layout
 #pragma unroll
-    for (int j = 0; j < KFWM; ++j) {
-      const int kf = frag(j);
+    for (int q = 0; q < NQ; ++q) {
+      const int kf = frag(2 * q);                          // even: the pair's first fragment
+      const bool in = kf + (c_ld >> 2) < F;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const unsigned row = (unsigned)(rg * MR + mb * 16 + 8 * h + r_ld);
+          hl[q][mb][h] = buffer_load16(hrs, in ? row * row_bytes + (unsigned)kf * 64u + (unsigned)c_ld * 16u : kOOB);
+        }
+#pragma unroll
+      for (int j = 2 * q; j < 2 * q + 2; ++j) {
+        ring[j] = buffer_load16(wrs, w_off(0, j));
+        __builtin_amdgcn_sched_barrier(0);  // slot order = issue order
+      }
+    }
+    static_assert((size_t)kWaves * NMB * 2048 <= lds_bytes(NMB), "the areas fit the kernel's LDS");
+    uint4* area = smem + wave * (NMB * 128);               // 2 KB per 16-row block
+    auto slot = [](int r, int c) { return r * 8 + (c ^ ((r >> 1) & 7)); };
+    const int r_mf = lane & 15, c_mf = lane >> 4;          // MFMA layout
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) area[mb * 128 + slot(8 * h + r_ld, c_ld)] = hl[q][mb][h];
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        const unsigned row = (unsigned)(rg * MR + mb * 16 + (lane & 15));
-        const unsigned off = row * row_bytes + (unsigned)kf * 64u + (lane >> 4) * 16u;
-        hreg[j][mb] = buffer_load16(hrs, kf < F ? off : kOOB);
+        hreg[2 * q][mb] = area[mb * 128 + slot(r_mf, c_mf)];
+        hreg[2 * q + 1][mb] = area[mb * 128 + slot(r_mf, 4 + c_mf)];
       }
-      ring[j] = buffer_load16(wrs, w_off(0, j));
-      __builtin_amdgcn_sched_barrier(0);  // slot order = issue order
     }
+    __syncthreads();   // the areas overlap the reduction buffers of the first tile
   }
 #pragma unroll
   for (int u = 1; u < G; ++u)
