@@ -1299,10 +1299,10 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int cur = ks & 1, nxt = cur ^ 1;
-        if (ks < 3) {
+        // fragments of the next K16 step: this stage's buffer, or at ks == 3 the next stage's,
+        // which the barrier at ks == 1 opened
 #pragma unroll
-          for (int vb = 0; vb < G::VB; ++vb) af[nxt][vb] = w_frag(u, vb, ks + 1);
-        }
+        for (int vb = 0; vb < G::VB; ++vb) af[nxt][vb] = ks < 3 ? w_frag(u, vb, ks + 1) : w_frag((u + 1) & 3, vb, 0);
 #pragma unroll
         for (int vb = 0; vb < G::VB; ++vb)
 #pragma unroll
@@ -1310,6 +1310,16 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
             acc[vb][hb] = mma32(af[cur][vb], hr[hp][ks][hb], (FIRST && u == 0 && ks == 0) ? f32x16{} : acc[vb][hb]);
 #pragma unroll
         for (int hb = 0; hb < G::HB; ++hb) hr[hp][ks][hb] = h_load(hso, ks, hb);   // G::HDepth stages ahead
+        // the fragment reads go out between the first MFMAs (into registers of their own), so
+        // their latency is covered by the rest of the step; the hidden loads reuse the
+        // registers the step's MFMAs read, so they come last
+#pragma unroll
+        for (int i = 0; i < G::VB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, G::VB * G::HB - G::VB, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, G::HB, 0);
         __builtin_amdgcn_sched_barrier(0);
         if (ks == 1) {
           // open the next stage: its W landed for every wavefront; buffer (u+3)&3 was last read
@@ -1320,10 +1330,6 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
           __builtin_amdgcn_sched_barrier(0);
           w_issue((u + 3) & 3, wso);
           __builtin_amdgcn_sched_barrier(0);
-        }
-        if (ks == 3) {                                    // next stage's first fragments
-#pragma unroll
-          for (int vb = 0; vb < G::VB; ++vb) af[nxt][vb] = w_frag((u + 1) & 3, vb, 0);
         }
       }
     }
