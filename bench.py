@@ -370,7 +370,8 @@ def main():
         roof["kernel"] = ("dlm::step_kernel with the top-k fold (the timed step also holds "
                           "finalize_topk_kernel)")
     elif wl.dtype == "bf16" and wl.B * wl.L > 64 and wl.H % 256 == 0:   # GEMM-shaped path
-        roof["kernel"] = "dlm::gemm_wide_kernel (the timed step also holds pack_hidden_kernel and finalize_kernel)"
+        gemm = "dlm::gemm_r512_kernel" if wl.B * wl.L > 256 else "dlm::gemm_r256_kernel"
+        roof["kernel"] = gemm + " (the timed step also holds pack_hidden_kernel and finalize_kernel)"
     else:
         roof["kernel"] = "dlm::step_kernel (one launch per step)"
     roof["algorithmic_bytes_per_launch"] = bytes_

@@ -40,7 +40,7 @@ constexpr int kTargetWorkgroups = 256;   // one per compute unit on MI355X
 
 // Launch geometry of one step, a pure function of the shapes (so the workspace size is too).
 struct Plan {
-  int gemm = 0;      // many rows: GEMM-shaped head + separate finalize kernel
+  int gemm = 0;      // many rows: GEMM-shaped head + separate finalize kernel (256 or 512: rows per group)
   int NMB = 0;       // 16-row blocks of hidden rows per workgroup (1, 2 or 4)
   int KFWM = 0;      // K fragments per wavefront per tile, rounded up (2, 8 or 16)
   int n_rg = 0;      // row groups
@@ -72,10 +72,12 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
   const int64_t m_pad = (M + 31) / 32 * 32;
   if (!topk && dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && m_pad * H * 2 < (1ll << 31)) {
-    // GEMM-shaped path: 256-row vocabulary tiles against 256-row groups; workgroups per row group
-    // a multiple of 8 where possible (so the groups of one tile can share an XCD)
-    const int64_t BN = dlm::GemmWide::BN;
-    const int64_t rows = dlm::GemmWide::Rows;
+    // GEMM-shaped path: 256-row vocabulary tiles against 256-row groups up to 256 rows, 128-row
+    // tiles against 512-row groups beyond; workgroups per row group a multiple of 8 where
+    // possible (so the groups of one tile can share an XCD)
+    const bool r512 = M > dlm::GemmR256::Rows;
+    const int64_t BN = r512 ? dlm::GemmR512::BN : dlm::GemmR256::BN;
+    const int64_t rows = r512 ? dlm::GemmR512::Rows : dlm::GemmR256::Rows;
     const int64_t nt = (V + BN - 1) / BN;
     const int64_t n_rg = (M + rows - 1) / rows;
     int64_t G_t = kTargetWorkgroups / n_rg;
@@ -84,7 +86,7 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
     if (G_t > nt) G_t = nt;
     if (G_t > dlm::kMaxVocabGroups) G_t = dlm::kMaxVocabGroups;
     if (n_rg * rows * G_t * 16 >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large");
-    p->gemm = 1;
+    p->gemm = (int)rows;
     p->n_rg = (int)n_rg;
     p->G_v = (int)G_t;
     p->ntiles = (int)nt;
@@ -267,10 +269,14 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     g.n_rg = p.n_rg;
     g.G_t = p.G_v;
     g.ntiles = p.ntiles;
-    const dim3 grid(p.n_rg * p.G_v), block(dlm::kGemmThreads);
-    const int rows = dlm::GemmWide::Rows;
-    const bool tail = a.V % dlm::GemmWide::BN != 0;
-    hipLaunchKernelGGL(tail ? dlm::gemm_wide_tail_kernel : dlm::gemm_wide_kernel, grid, block, 0, stream, g);
+    const bool r512 = p.gemm == dlm::GemmR512::Rows;
+    const dim3 grid(p.n_rg * p.G_v), block(r512 ? dlm::GemmR512::Threads : dlm::GemmR256::Threads);
+    const int rows = p.gemm;
+    const bool tail = a.V % (r512 ? dlm::GemmR512::BN : dlm::GemmR256::BN) != 0;
+    if (r512)
+      hipLaunchKernelGGL(tail ? dlm::gemm_r512_tail_kernel : dlm::gemm_r512_kernel, grid, block, 0, stream, g);
+    else
+      hipLaunchKernelGGL(tail ? dlm::gemm_r256_tail_kernel : dlm::gemm_r256_kernel, grid, block, 0, stream, g);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "gemm kernel launch: %s", hipGetErrorString(e));
     hipLaunchKernelGGL(dlm::finalize_kernel, dim3(c.B), dim3(dlm::kThreads), 0, stream, a.c, a.partials, p.G_v,

@@ -1034,32 +1034,42 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
 // ascending vocabulary order, folded into that row's running statistics at the end of the tile.
 // Each workgroup ends with one record per row; finalize_kernel merges them and commits.
 // ----------------------------------------------------------------------------------------------
-constexpr int kGemmWaves = 4;
-constexpr int kGemmThreads = kGemmWaves * 64;
 constexpr int kGemmBK = 64;                               // K per stage
 constexpr int kGemmRing = 4;                              // W stage buffers in LDS
 
-// Tile shape: a wavefront owns VB 32-row vocabulary blocks x HB 32-row hidden blocks (VB * HB = 16
-// accumulator blocks = 256 AGPRs).  The shape in use is 8 x 2: few hidden rows per wavefront make
-// its hidden fragments a small register cost per stage of lead (measured against 4 x 4, which
-// reads each W fragment for 4 products instead of 2: as fast at 512 rows, slower at 256).
-template <int VB_, int HB_>
+// Tile shape: WAVES wavefronts, each owning VB 32-row vocabulary blocks x HB 32-row hidden blocks
+// (VB * HB * WAVES = 64 accumulator blocks: every accumulator register of the CU's four SIMDs).
+// Two shapes are built, both with 64 hidden rows per wavefront (few hidden rows make its hidden
+// fragments a small register cost per stage of lead; 4 x 4 blocks, which read each W fragment
+// for 4 products instead of 2, measured as fast at 512 rows and slower at 256):
+//   * GemmR256: 4 wavefronts (one per SIMD, 256 accumulator registers each) x 8 x 2 blocks:
+//     256 vocabulary rows per tile against a 256-row group;
+//   * GemmR512: 8 wavefronts (two per SIMD, 128 accumulator registers each) x 4 x 2 blocks: 128
+//     vocabulary rows per tile against a 512-row group.  While one wavefront of a SIMD folds its
+//     statistics or waits, the other keeps the matrix core busy; each hidden fragment is read
+//     for half as many products.  Used above 256 rows (below, most of a 512-row group is
+//     padding).
+template <int VB_, int HB_, int WAVES_>
 struct GemmShape {
-  static constexpr int VB = VB_, HB = HB_;
+  static constexpr int VB = VB_, HB = HB_, Waves = WAVES_, Threads = 64 * WAVES_;
   static constexpr int BN = 32 * VB;                      // vocabulary rows per tile
   static constexpr int RowsPerWave = 32 * HB;
-  static constexpr int Rows = kGemmWaves * RowsPerWave;   // hidden rows per row group
+  static constexpr int Rows = Waves * RowsPerWave;        // hidden rows per row group
   static constexpr int Slot = BN * 8;                     // 16-byte slots per W stage buffer
-  static constexpr int WDma = BN / 8 / kGemmWaves;        // W load instructions per wavefront per stage
+  static constexpr int WDma = BN / 8 / Waves;             // W load instructions per wavefront per stage
   static constexpr int HDepth = 4 / HB;                   // stages of hidden fragments in flight (64 VGPRs)
   // vector-memory instructions issued after a stage's W loads and before the wait that must cover
   // them: the rest of that stage (2 K16 steps of hidden loads), one whole stage (4 K16 steps of
   // hidden loads + the next W loads) and the first half of the following one
   static constexpr int VmAfterW = 2 * HB + (4 * HB + WDma) + 2 * HB;
-  static_assert(VB * HB == 16, "256 accumulator registers");
+  static_assert(VB * HB * Waves == 64, "every accumulator register of the SIMDs");
   static_assert(VmAfterW <= 63, "vmcnt holds at most 63");
+  // the prologue's first W stage has the other two prologue stages and every prologue hidden
+  // load behind it, at least as many as the steady-state wait counts on
+  static_assert(2 * WDma + HDepth * 4 * HB >= VmAfterW, "prologue wait covers W stage 0");
 };
-using GemmWide = GemmShape<8, 2>;
+using GemmR256 = GemmShape<8, 2, 4>;
+using GemmR512 = GemmShape<4, 2, 8>;
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
@@ -1185,7 +1195,7 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
   // buffer being filled from the one being read (it would otherwise wait for every fill)
   __shared__ uint4 wring0[G::Slot], wring1[G::Slot], wring2[G::Slot], wring3[G::Slot];
   auto ring = [&](int slot) -> uint4* { return slot == 0 ? wring0 : slot == 1 ? wring1 : slot == 2 ? wring2 : wring3; };
-  __shared__ float4 st_lds[kGemmWaves * G::HB * 64];  // running statistics, [wave][hb][lane]
+  __shared__ float4 st_lds[G::Waves * G::HB * 64];    // running statistics, [wave][hb][lane]
   const int tid = lid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroups of one vocabulary range (one per row group) sit 8 block indices apart: one XCD
@@ -1364,8 +1374,10 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
 }
 
 // One kernel per tail handling (plain kernels, so both compilation passes see them)
-__global__ __launch_bounds__(kGemmThreads) void gemm_wide_kernel(const GemmArgs a) { gemm_stats<GemmWide, false>(a); }
-__global__ __launch_bounds__(kGemmThreads) void gemm_wide_tail_kernel(const GemmArgs a) { gemm_stats<GemmWide, true>(a); }
+__global__ __launch_bounds__(GemmR256::Threads) void gemm_r256_kernel(const GemmArgs a) { gemm_stats<GemmR256, false>(a); }
+__global__ __launch_bounds__(GemmR256::Threads) void gemm_r256_tail_kernel(const GemmArgs a) { gemm_stats<GemmR256, true>(a); }
+__global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_kernel(const GemmArgs a) { gemm_stats<GemmR512, false>(a); }
+__global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_tail_kernel(const GemmArgs a) { gemm_stats<GemmR512, true>(a); }
 
 // Merge + commit after the GEMM-path kernel: one workgroup per sequence.
 __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, const float4* records, int G,

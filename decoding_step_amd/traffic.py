@@ -7,7 +7,7 @@ factor between each counter's units and bytes.  The result is written as JSON ne
 the summaries under ``profiles/``, tagged with a hash of the kernel sources and build
 flags; ``bench.py`` reports it as ``roofline.traffic`` only while that hash matches.
 
-    python -m decoding_step_amd.traffic --workload mixed_b16_l32 --kernel gemm_wide_kernel \\
+    python -m decoding_step_amd.traffic --workload mixed_b16_l32 --kernel gemm_r512_kernel \\
         --fetch prof/pmc_FETCH --write prof/pmc_WRITE \\
         --copy-fetch prof/pmc_copy_FETCH --copy-write prof/pmc_copy_WRITE
 """

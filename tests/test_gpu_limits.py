@@ -2,7 +2,7 @@
 
 Every row goes through the head on the GPU; the oracle recomputes a sample of rows (first and
 last of every row group among them), which it can afford at these sizes.  Shapes: the largest
-B and L (16384 rows, the GEMM path with 64 row groups), the largest B with L = 1, the largest
+B and L (16384 rows, the GEMM path with 32 row groups of 512), the largest B with L = 1, the largest
 hidden size on the streaming and on the GEMM path, and a one-token vocabulary on the GEMM path.
 """
 import numpy as np
@@ -34,7 +34,7 @@ def _sample_rows(M, n=40, group=256, seed=3):
 
 
 @pytest.mark.parametrize("B,L,H,V", [
-    (256, 64, 2048, 30011),    # the largest block batch: 16384 rows, GEMM path, 64 row groups
+    (256, 64, 2048, 30011),    # the largest block batch: 16384 rows, GEMM path, 32 row groups
     (256, 1, 1024, 20011),     # the largest B with L = 1 (256 rows)
     (1, 8, 4096, 5003),        # the largest hidden size of the streaming kernel (bf16)
     (9, 32, 4096, 5003),       # the GEMM path at H = 4096

@@ -135,14 +135,15 @@ def _stats_inputs(M, H, V, dtype, seed):
     (1, 3, 32, 17, "bf16"),         # fewer tiles than wavefronts
     (1, 2, 32, 1, "bf16"),          # one-token vocabulary
     (1, 16, 2048, 20011, "bf16"),   # full hidden size, prime vocabulary
-    (5, 13, 256, 3001, "bf16"),     # GEMM path: 65 rows, ragged last tile
-    (4, 30, 256, 1000, "bf16"),     # GEMM path: 120 rows, fewer tiles than workgroups
+    (5, 13, 256, 3001, "bf16"),     # GEMM path, 256-row groups: 65 rows, ragged last tile
+    (4, 30, 256, 1000, "bf16"),     # GEMM path, 256-row groups: 120 rows, fewer tiles than workgroups
     (8, 32, 256, 30011, "bf16"),    # GEMM path: a full 256-row group, ragged last tile
-    (17, 31, 512, 5003, "bf16"),    # GEMM path: 527 rows = three 256-row groups
+    (17, 31, 512, 5003, "bf16"),    # GEMM path, 512-row groups: 527 rows = two groups, 40 workgroups each
     (5, 13, 128, 3001, "bf16"),     # 65 rows with H % 256 != 0: streaming kernel, row groups
-    (16, 32, 2048, 30011, "bf16"),  # GEMM path at the batched workload's row count
-    (9, 32, 512, 40013, "bf16"),    # GEMM path: 2 groups paired on one XCD, second 32 rows deep
-    (16, 32, 256, 65613, "bf16"),   # GEMM path: 2 full groups paired on one XCD, ragged last tile
+    (16, 32, 2048, 30011, "bf16"),  # GEMM path at the batched workload's row count (one 512-row group)
+    (9, 32, 512, 40013, "bf16"),    # GEMM path: 288 rows, one 512-row group mostly padding
+    (16, 32, 256, 65613, "bf16"),   # GEMM path: a full 512-row group, ragged last tile
+    (24, 32, 256, 30011, "bf16"),   # GEMM path: 768 rows = 2 groups paired on one XCD, ragged tile
 ])
 def test_token_stats_against_oracle(B, L, H, V, dtype):
     M = B * L
