@@ -325,6 +325,13 @@ __device__ __forceinline__ float4 record_load(__amdgpu_buffer_rsrc_t r, unsigned
   return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kDeviceCoherent));
 }
 
+// Records written by an earlier kernel on the stream: the kernel boundary already makes them
+// visible to every compute unit, so an ordinary load serves, and neighbouring records come in
+// whole cache lines through L2 instead of one 16-byte device-scope read each.
+__device__ __forceinline__ float4 record_load_after_kernel(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
 __device__ __forceinline__ float4 stats_pack(const Stats& a) {
   return make_float4(a.m1, a.s, __int_as_float(a.id), a.m2);
 }
@@ -633,6 +640,9 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 //     (merge_records' tree, four rows per wavefront at once).
 //   GROUPED = true: `rec` holds the second-level records of the distributed merge, G <= kGroup per
 //     row at r*rs_row + g; one 16-lane row per row of the block (the second level of the same tree).
+// IN_KERNEL: `rec` may have been written by other workgroups of the running kernel (or outside
+// this library's kernels): device-scope loads; otherwise an earlier kernel of this library on the
+// stream wrote it and ordinary loads serve.
 // conf / token go to LDS, then one wavefront per sequence commits.  With c.out_records the merged
 // record itself is written instead (ids offset by c.v_begin) and nothing commits.
 // `pre` is the state this wavefront already fetched for sequence `pre_b` (or pre_b = -1).
@@ -656,7 +666,7 @@ __device__ __forceinline__ void finalize_row(const CommitArgs& c, const Stats& t
   s_gap[rr] = t.m1 - t.m2;
 }
 
-template <bool GROUPED>
+template <bool GROUPED, bool IN_KERNEL>
 __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t rec, int G, int rs_row, int rs_g,
                                    int b_begin, int b_end, uint4* smem, const SeqState& pre, int pre_b) {
   const int tid = lid(), lane = tid & 63;
@@ -677,7 +687,8 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
       Stats t;
       if (GROUPED || G <= kGroup) {
         // at most one group: record j in lane j, one 16-lane tree
-        float4 v = record_load(rec, j < G ? src + 16u * (unsigned)(j * rs_g) : 0x80000000u);
+        const unsigned o = j < G ? src + 16u * (unsigned)(j * rs_g) : 0x80000000u;
+        float4 v = IN_KERNEL ? record_load(rec, o) : record_load_after_kernel(rec, o);
         v = j < G ? v : stats_pack(stats_empty());
         t = stats_row16_merge(stats_unpack(v));
       } else {
@@ -686,7 +697,8 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
 #pragma unroll
         for (int k = 0; k < kGroup; ++k) {
           const int g = kGroup * j + k;
-          v[k] = record_load(rec, g < G ? src + 16u * (unsigned)(g * rs_g) : 0x80000000u);
+          const unsigned o = g < G ? src + 16u * (unsigned)(g * rs_g) : 0x80000000u;
+          v[k] = IN_KERNEL ? record_load(rec, o) : record_load_after_kernel(rec, o);
         }
         Stats q[kGroup];
 #pragma unroll
@@ -1002,7 +1014,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  finalize_sequences<true>(c, l2, a.nq, a.nq, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1);
+  finalize_sequences<true, true>(c, l2, a.nq, a.nq, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1);
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -1390,7 +1402,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, 
   SeqState pre;
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   if (do_commit && wave == 0) pre = load_seq_state(c, b);
-  finalize_sequences<false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  finalize_sequences<false, false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // Top-k export of one row (one wavefront).  Lane l holds the row's best-first lists g = l, l + 64,
@@ -1452,7 +1464,7 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
     SeqState pre;
     const bool do_commit = (c.flags & kFlagCommit) != 0;
     if (do_commit && wave == 0) pre = load_seq_state(c, b);
-    finalize_sequences<false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
+    finalize_sequences<false, false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
     return;
   }
   const int row = (gid() - c.B) * kWaves + wave;
@@ -1466,11 +1478,11 @@ __global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArg
 #pragma unroll
   for (int n = 0; n < N; ++n) {
     const int gs = record_of_lane(lane, n);   // statistics: merge_records' layout
-    r[n] = record_load(rec, gs < G ? (unsigned)(((size_t)row * G + gs) * 16) : kOOB);
+    r[n] = record_load_after_kernel(rec, gs < G ? (unsigned)(((size_t)row * G + gs) * 16) : kOOB);
     const int g = lane + 64 * n;              // lists: any layout (they merge by value)
 #pragma unroll
     for (int j = 0; j < kTopK / 2; ++j)
-      e[n][j] = record_load(trec, g < G ? (unsigned)(((size_t)row * G + g) * (kTopK * 8) + 16 * j) : kOOB);
+      e[n][j] = record_load_after_kernel(trec, g < G ? (unsigned)(((size_t)row * G + g) * (kTopK * 8) + 16 * j) : kOOB);
   }
   TopK t[N];
 #pragma unroll
@@ -1500,7 +1512,9 @@ __global__ __launch_bounds__(kThreads) void merge_commit_kernel(const CommitArgs
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, G * M * 16, 0x00020000);
   SeqState pre;
   if (wave == 0) pre = load_seq_state(c, b);
-  finalize_sequences<false>(c, rec, G, 1, M, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  // (the gathered records may have been written by a copy or by another device: device-scope
+  // loads, as in the in-kernel merge)
+  finalize_sequences<false, true>(c, rec, G, 1, M, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // dlm_commit: conf / tokens given, one wavefront per sequence.
