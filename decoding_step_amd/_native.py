@@ -49,7 +49,8 @@ class dlm_policy(ctypes.Structure):
                 ("stream", ctypes.c_void_p),
                 ("out_conf", ctypes.c_void_p), ("out_gap", ctypes.c_void_p),
                 ("seq_done", ctypes.c_void_p),
-                ("topk", ctypes.c_int32), ("out_topk_tokens", ctypes.c_void_p), ("out_topk_prob", ctypes.c_void_p)]
+                ("topk", ctypes.c_int32), ("out_topk_tokens", ctypes.c_void_p), ("out_topk_prob", ctypes.c_void_p),
+                ("head_events", ctypes.c_void_p * 2)]
 
 
 class DlmError(RuntimeError):
@@ -166,6 +167,19 @@ class StepPolicy:
         self.c.out_topk_tokens = _ptr(out_topk_tokens)
         self.c.out_topk_prob = _ptr(out_topk_prob)
         self._keep_topk = (out_topk_tokens, out_topk_prob)
+
+    def set_head_events(self, begin=None, end=None) -> None:
+        """Events recorded right before / after the vocabulary-head kernel (``head_events``):
+        ``torch.cuda.Event(enable_timing=True)`` objects or raw ``hipEvent_t`` handles, or None."""
+        def handle(ev):
+            if ev is None or isinstance(ev, int):
+                return ev or None
+            if not ev.cuda_event:          # torch creates the event at its first record
+                ev.record()
+            return ev.cuda_event
+        self.c.head_events[0] = handle(begin)
+        self.c.head_events[1] = handle(end)
+        self._keep_events = (begin, end)
 
     def set_outputs(self, out_conf=None, out_gap=None) -> None:
         self.c.out_conf = _ptr(out_conf)

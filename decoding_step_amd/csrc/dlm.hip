@@ -13,7 +13,7 @@
 #include "dlm_device.hpp"
 
 static_assert(sizeof(dlm_shard_record) == 16, "a shard record is one 16-byte statistics record");
-static_assert(sizeof(dlm_seq_policy) == 20 && sizeof(dlm_policy) == 120 && sizeof(dlm_credit_slot) == 8,
+static_assert(sizeof(dlm_seq_policy) == 20 && sizeof(dlm_policy) == 136 && sizeof(dlm_credit_slot) == 8,
               "C ABI struct layout (the Python binding mirrors it)");
 
 namespace {
@@ -221,7 +221,17 @@ int check_topk(const dlm_policy* pol, dlm::CommitArgs* c) {
   return DLM_OK;
 }
 
-int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::CommitArgs c, bool commit) {
+// Records policy->head_events[i] (if set) on the stream: i = 0 before the kernel that streams W,
+// i = 1 after it.  Only for calls that time the head (time_head).
+int head_event(const dlm_policy* pol, bool time_head, int i, hipStream_t stream) {
+  if (!time_head || !pol->head_events[i]) return DLM_OK;
+  const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(pol->head_events[i]), stream);
+  if (e != hipSuccess) return fail(DLM_ERR_HIP, "head_events[%d] record: %s", i, hipGetErrorString(e));
+  return DLM_OK;
+}
+
+int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::CommitArgs c, bool commit,
+             bool time_head) {
   Plan p;
   int rc = make_plan(pol->B, pol->L, pol->H, pol->V, pol->dtype, c.topk, &p);
   if (rc) return rc;
@@ -273,12 +283,14 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     const dim3 grid(p.n_rg * p.G_v), block(r512 ? dlm::GemmR512::Threads : dlm::GemmR256::Threads);
     const int rows = p.gemm;
     const bool tail = a.V % (r512 ? dlm::GemmR512::BN : dlm::GemmR256::BN) != 0;
+    if ((rc = head_event(pol, time_head, 0, stream))) return rc;
     if (r512)
       hipLaunchKernelGGL(tail ? dlm::gemm_r512_tail_kernel : dlm::gemm_r512_kernel, grid, block, 0, stream, g);
     else
       hipLaunchKernelGGL(tail ? dlm::gemm_r256_tail_kernel : dlm::gemm_r256_kernel, grid, block, 0, stream, g);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "gemm kernel launch: %s", hipGetErrorString(e));
+    if ((rc = head_event(pol, time_head, 1, stream))) return rc;
     hipLaunchKernelGGL(dlm::finalize_kernel, dim3(c.B), dim3(dlm::kThreads), 0, stream, a.c, a.partials, p.G_v,
                        p.n_rg * rows);
     e = hipGetLastError();
@@ -286,8 +298,10 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     return ok();
   }
   if (p.topk) {
+    if ((rc = head_event(pol, time_head, 0, stream))) return rc;
     rc = pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, true>(a, p, stream) : launch_step_for<float, true>(a, p, stream);
     if (rc) return rc;
+    if ((rc = head_event(pol, time_head, 1, stream))) return rc;
     const int rows = 16 * p.NMB;
     const int M = a.M;
     const int grid = c.B + (M + dlm::kWaves - 1) / dlm::kWaves;
@@ -297,7 +311,10 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "top-k finalize kernel launch: %s", hipGetErrorString(e));
     return ok();
   }
-  return pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, false>(a, p, stream) : launch_step_for<float, false>(a, p, stream);
+  if ((rc = head_event(pol, time_head, 0, stream))) return rc;
+  rc = pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, false>(a, p, stream) : launch_step_for<float, false>(a, p, stream);
+  if (rc) return rc;
+  return head_event(pol, time_head, 1, stream);
 }
 
 }  // namespace
@@ -324,7 +341,7 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
   c.out_commit = out_commit;
   c.out_conf = policy->out_conf;
   c.out_gap = policy->out_gap;
-  return run_step(hidden, W_vocab, policy, c, true);
+  return run_step(hidden, W_vocab, policy, c, true, true);
 }
 
 int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mask_state,
@@ -360,7 +377,7 @@ int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mas
       c.out_topk_tokens = topk_tokens0 + (size_t)n * rows * c.topk;
       c.out_topk_prob = topk_prob0 ? topk_prob0 + (size_t)n * rows * c.topk : nullptr;
     }
-    rc = run_step(static_cast<const char*>(hidden_steps) + n * step_bytes, W_vocab, policy, c, true);
+    rc = run_step(static_cast<const char*>(hidden_steps) + n * step_bytes, W_vocab, policy, c, true, false);
     if (rc) return rc;  // only a failed launch can get here, after validation passed
   }
   return ok();
@@ -378,7 +395,7 @@ int dlm_token_stats(const void* hidden, const void* W_vocab, const dlm_policy* p
   c.out_tokens = out_tokens;
   c.out_conf = out_conf;
   c.out_gap = out_gap;
-  return run_step(hidden, W_vocab, policy, c, false);
+  return run_step(hidden, W_vocab, policy, c, false, true);
 }
 
 int dlm_shard_stats(const void* hidden, const void* W_shard, int64_t v_begin, const dlm_policy* policy,
@@ -394,7 +411,7 @@ int dlm_shard_stats(const void* hidden, const void* W_shard, int64_t v_begin, co
   std::memset(&c, 0, sizeof c);
   c.out_records = reinterpret_cast<float4*>(out_records);
   c.v_begin = (int)v_begin;
-  return run_step(hidden, W_shard, policy, c, false);
+  return run_step(hidden, W_shard, policy, c, false, false);
 }
 
 int dlm_merge_commit(const dlm_shard_record* records, int64_t n_shards, uint8_t* mask_state,

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define DLM_VERSION_STRING "0.4.0"
+#define DLM_VERSION_STRING "0.5.0"
 
 #define DLM_MAX_SEQS 256   /* sequences per call                                  */
 #define DLM_MAX_L 64       /* positions per block: one wavefront lane per position */
@@ -123,7 +123,18 @@ typedef struct {
   int32_t topk;              /* top-k export: 0 = off, 1..DLM_MAX_TOPK candidates per row   */
   int32_t* out_topk_tokens;  /* device [B][L][topk] int32 when topk > 0 (see below)         */
   float* out_topk_prob;      /* optional device [B][L][topk] float, or NULL                 */
+  void* head_events[2];      /* optional hipEvent_t pair, each may be NULL (see below)      */
 } dlm_policy;
+
+/*
+ * Timing the vocabulary head alone (dlm_decode_step and dlm_token_stats; the other calls ignore
+ * the field).  head_events[0] is recorded on the stream right before the launch of the kernel
+ * that streams W_vocab, head_events[1] right after it: the step kernel itself up to 64 rows (it
+ * also merges and commits), the GEMM-shaped head beyond (between the hidden-row packing and the
+ * merge + commit kernel).  The events are the caller's (created with hipEventCreate or a
+ * framework's event type); hipEventElapsedTime of the pair is that kernel's duration.  A failed
+ * record returns DLM_ERR_HIP.
+ */
 
 /*
  * Top-k candidate export (policy->topk > 0; dlm_decode_step, dlm_decode_steps and

@@ -51,7 +51,7 @@ def test_header_constants_match_binding():
     assert ctypes.sizeof(nat.dlm_credit_slot) == 8
     assert ctypes.sizeof(nat.dlm_shard_record) == 16
     assert ctypes.sizeof(nat.dlm_seq_policy) == 20       # the library asserts the same sizes
-    assert ctypes.sizeof(nat.dlm_policy) == 120
+    assert ctypes.sizeof(nat.dlm_policy) == 136
 
 
 def test_workspace_sizes():
