@@ -680,6 +680,28 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
     const int b1 = min(b_end, b0 + seq_per_stage);
     const int r_first = b0 * c.L, nrows = (b1 - b0) * c.L;
     // 4 rows per wavefront pass, one per 16-lane row; lane j of a row takes group j
+    if constexpr (GROUPED) {
+      // one record per lane: two passes per iteration, both loads before the first merge, so
+      // up to 64 rows cost one round trip
+      for (int rr0 = wave * 4; rr0 < nrows; rr0 += 2 * kWaves * 4) {
+        const int j = lane & 15;
+        float4 v[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rr = rr0 + h * kWaves * 4 + (lane >> 4);
+          const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
+          const unsigned o = j < G && rr < nrows ? src + 16u * (unsigned)(j * rs_g) : 0x80000000u;
+          v[h] = IN_KERNEL ? record_load(rec, o) : record_load_after_kernel(rec, o);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int rr = rr0 + h * kWaves * 4 + (lane >> 4);
+          if (rr0 + h * kWaves * 4 >= nrows) break;   // (uniform: no row of this pass exists)
+          const Stats t = stats_row16_merge(stats_unpack(j < G ? v[h] : stats_pack(stats_empty())));
+          if (rr < nrows && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
+        }
+      }
+    } else
     for (int rr0 = wave * 4; rr0 < nrows; rr0 += kWaves * 4) {
       const int rr = rr0 + (lane >> 4), j = lane & 15;
       const bool rin = rr < nrows;
@@ -990,11 +1012,24 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   if (!s_last) return;
   const __amdgpu_buffer_rsrc_t l2 = __builtin_amdgcn_make_buffer_rsrc(a.level2, 0, a.n_rg * MR * a.nq * 16, 0x00020000);
-  for (int rr = wave * 4 + (lane >> 4); rr < MR; rr += kWaves * 4) {   // 4 rows per wavefront pass
+  // 4 rows per wavefront pass; every pass's load is issued before the first merge, so the
+  // passes (two at 64 rows) share one round trip to the coherence point
+  constexpr int kPasses = (MR + kWaves * 4 - 1) / (kWaves * 4);
+  float4 gv_rec[kPasses];
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int rr = pass * kWaves * 4 + wave * 4 + (lane >> 4);
     const int j = lane & 15, g = kGroup * grp + j;
     const unsigned row = (unsigned)(rg * MR + rr);
-    float4 v = record_load(rec, g < a.G_v ? (row * (unsigned)a.G_v + (unsigned)g) * 16u : 0x80000000u);
-    v = g < a.G_v ? v : stats_pack(stats_empty());
+    gv_rec[pass] = record_load(rec, g < a.G_v && rr < MR ? (row * (unsigned)a.G_v + (unsigned)g) * 16u : 0x80000000u);
+  }
+#pragma unroll
+  for (int pass = 0; pass < kPasses; ++pass) {
+    const int rr = pass * kWaves * 4 + wave * 4 + (lane >> 4);
+    if (rr >= MR) continue;                   // (uniform over the row's 16 lanes)
+    const int j = lane & 15, g = kGroup * grp + j;
+    const unsigned row = (unsigned)(rg * MR + rr);
+    const float4 v = g < a.G_v ? gv_rec[pass] : stats_pack(stats_empty());
     const Stats t = stats_row16_merge(stats_unpack(v));
     if (j == 0) record_store(l2, (row * (unsigned)a.nq + (unsigned)grp) * 16u, stats_pack(t));
   }
