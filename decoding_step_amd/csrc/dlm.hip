@@ -91,7 +91,7 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
     p->G_v = (int)G_t;
     p->ntiles = (int)nt;
     p->lds = 0;
-    // ticket | records [n_rg * rows][G_t] | hidden rows in fragment order, padded to 32 rows
+    // ticket | records [G_t][n_rg * rows] | hidden rows in fragment order, padded to 32 rows
     p->packed_off = kTicketBytes + (size_t)n_rg * rows * G_t * 16;
     p->packed_bytes = (size_t)m_pad * H * 2;
     p->ws = p->packed_off + p->packed_bytes;

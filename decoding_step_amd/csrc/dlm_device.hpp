@@ -1123,7 +1123,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 struct GemmArgs {
   const void* hidden_packed;  // fragment-ordered hidden rows (pack_hidden_kernel), zero-padded to 32 rows
   const void* W;              // [V][H] bf16
-  float4* records;            // [n_rg * rows per group][G_t]
+  float4* records;            // [G_t][n_rg * rows per group]: each workgroup's records in one run
   int H, V, M;
   int n_rg;                   // row groups
   int G_t;                    // workgroups per row group
@@ -1416,7 +1416,7 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
     row_swap<32>(sh.id, x0, x1);                 lo.id = x0;                 hi.id = x1;
     const Stats t = stats_merge(lo, hi);
     const unsigned row = h_row0 + 32u * hb;
-    if (lane < 32 && (int)row < a.M) a.records[(size_t)row * a.G_t + gi] = stats_pack(t);
+    if (lane < 32 && (int)row < a.M) a.records[(size_t)gi * (a.n_rg * G::Rows) + row] = stats_pack(t);
   }
 }
 
@@ -1437,7 +1437,9 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, 
   SeqState pre;
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   if (do_commit && wave == 0) pre = load_seq_state(c, b);
-  finalize_sequences<false, false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  // records [G][nrows_total] (the GEMM kernels write each workgroup's records as one run): a
+  // load instruction of the merge reads 16-byte records of 4 consecutive rows per record index
+  finalize_sequences<false, false>(c, rec, G, 1, nrows_total, b, b + 1, stage, pre, wave == 0 ? b : -1);
 }
 
 // Top-k export of one row (one wavefront).  Lane l holds the row's best-first lists g = l, l + 64,
