@@ -122,11 +122,15 @@ def test_decode_steps_equals_single_steps_and_oracle(name, n, sample):
     assert compared >= 2
 
 
-def test_decode_steps_inside_a_graph():
-    say("gpu: dlm_decode_steps captured in a HIP graph, replayed 3 times")
+@pytest.mark.parametrize("name", [
+    "credit_b1_l32",        # streaming kernel: one launch per step
+    "mixed_b16_l32",        # GEMM path: pack, head and finalize kernels per step
+])
+def test_decode_steps_inside_a_graph(name):
+    say(f"gpu: dlm_decode_steps {name} captured in a HIP graph, replayed 3 times")
     from decoding_step_amd.device import credit_tokens, credit_values, new_credit, to_device
     n = 4
-    wl, W, Wd, seq, dec = _setup("credit_b1_l32")
+    wl, W, Wd, seq, dec = _setup(name)
     h_np, _, _, _ = _stage_one_by_one(wl, W, dec, n)
     hidden_steps = to_device(h_np.reshape(n, wl.B, wl.L, wl.H))
     ref_tok, ref_com, ref_final = _run_steps(wl, dec, hidden_steps)
