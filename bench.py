@@ -391,7 +391,7 @@ def main():
                           "finalize_topk_kernel)")
     elif gemm_path:
         gemm = "dlm::gemm_r512_kernel" if wl.B * wl.L > 256 else "dlm::gemm_r256_kernel"
-        roof["kernel"] = gemm + " (the step also holds pack_hidden_kernel and finalize_kernel)"
+        roof["kernel"] = gemm + " (the step also holds pack_hidden_kernel and finalize_parts_kernel)"
     else:
         roof["kernel"] = "dlm::step_kernel (one launch per step)"
     if head is not None:

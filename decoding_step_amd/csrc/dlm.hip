@@ -49,6 +49,7 @@ struct Plan {
   size_t lds = 0;    // dynamic LDS bytes
   size_t ws = 0;     // workspace bytes
   size_t packed_off = 0, packed_bytes = 0;  // GEMM path: fragment-ordered hidden rows in the workspace
+  size_t rowout_off = 0;                    // GEMM path: published per-row conf / token / gap [B*L]
   int topk = 0;      // streaming kernel with the top-k fold + finalize_topk_kernel
   size_t topk_off = 0;                      // top-k records in the workspace
   int nq = 0;        // streaming kernel: groups of dlm::kGroup vocabulary ranges (two-level merge)
@@ -91,10 +92,13 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
     p->G_v = (int)G_t;
     p->ntiles = (int)nt;
     p->lds = 0;
-    // ticket | records [G_t][n_rg * rows] | hidden rows in fragment order, padded to 32 rows
-    p->packed_off = kTicketBytes + (size_t)n_rg * rows * G_t * 16;
+    // per-sequence counters [B] (padded to 256 bytes) | records [G_t][n_rg * rows] | hidden rows
+    // in fragment order, padded to 32 rows | published per-row values [B*L] x 16 bytes
+    p->ticket_bytes = (size_t)((4 * B + 255) / 256 * 256);
+    p->packed_off = p->ticket_bytes + (size_t)n_rg * rows * G_t * 16;
     p->packed_bytes = (size_t)m_pad * H * 2;
-    p->ws = p->packed_off + p->packed_bytes;
+    p->rowout_off = p->packed_off + p->packed_bytes;
+    p->ws = p->rowout_off + (size_t)M * 16;
     return DLM_OK;
   }
   // each wavefront holds ceil(F / 8) hidden fragments per 16-row block in registers
@@ -291,8 +295,10 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "gemm kernel launch: %s", hipGetErrorString(e));
     if ((rc = head_event(pol, time_head, 1, stream))) return rc;
-    hipLaunchKernelGGL(dlm::finalize_kernel, dim3(c.B), dim3(dlm::kThreads), 0, stream, a.c, a.partials, p.G_v,
-                       p.n_rg * rows);
+    const int parts = (c.L + dlm::kFinRows - 1) / dlm::kFinRows;
+    hipLaunchKernelGGL(dlm::finalize_parts_kernel, dim3(c.B * parts), dim3(128), 0, stream, a.c, a.partials,
+                       p.G_v, p.n_rg * rows, a.ticket,
+                       reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.rowout_off));
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "finalize kernel launch: %s", hipGetErrorString(e));
     return ok();

@@ -1079,7 +1079,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
 // Lane l of acc[vb][hb] register r holds vocabulary row 32vb + 8(r/4) + 4(l/32) + r%4 of the tile
 // against hidden row 32hb + l%32 of the wavefront: 16 VB logits of one row per lane and tile, in
 // ascending vocabulary order, folded into that row's running statistics at the end of the tile.
-// Each workgroup ends with one record per row; finalize_kernel merges them and commits.
+// Each workgroup ends with one record per row; finalize_parts_kernel merges them and commits.
 // ----------------------------------------------------------------------------------------------
 constexpr int kGemmBK = 64;                               // K per stage
 constexpr int kGemmRing = 4;                              // W stage buffers in LDS
@@ -1426,20 +1426,84 @@ __global__ __launch_bounds__(GemmR256::Threads) void gemm_r256_tail_kernel(const
 __global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_kernel(const GemmArgs a) { gemm_stats<GemmR512, false>(a); }
 __global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_tail_kernel(const GemmArgs a) { gemm_stats<GemmR512, true>(a); }
 
-// Merge + commit after the GEMM-path kernel: one workgroup per sequence.
-__global__ __launch_bounds__(kThreads) void finalize_kernel(const CommitArgs c, const float4* records, int G,
-                                                            int nrows_total) {
-  __shared__ uint4 stage[kRowsPerStage * 12 / 16];
-  const int b = gid();
-  const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
+// Merge + commit after the GEMM-path kernel, spread over more compute units: workgroup
+// (b, part) merges rows kFinRows*part .. +kFinRows-1 of sequence b (two wavefronts of four rows,
+// one 16-lane row each, the tree of finalize_sequences: the same bits), then
+//   * without a commit, writes those rows' outputs (or, for a vocabulary shard, their merged
+//     records with global ids) and ends;
+//   * with one, publishes conf / token / gap of its rows at device scope, and the last part of the
+//     sequence to finish (a wrapping counter per sequence, so a zeroed workspace is zero again
+//     after every call) commits the sequence from the published values.
+// records: [G][nrows_total] (the GEMM kernels' layout).  Grid: B x ceil(L / kFinRows) workgroups of
+// 128 threads.  tickets: [B] counters; row_out: [B*L] 16-byte values.
+constexpr int kFinRows = 8;
+__global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c, const float4* records, int G,
+                                                             int nrows_total, unsigned* tickets,
+                                                             float4* row_out) {
+  constexpr unsigned kOOB = 0x80000000u;
+  const int parts = (c.L + kFinRows - 1) / kFinRows;
+  const int b = gid() / parts, part = gid() % parts;
+  const int tid = lid(), lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool do_commit = (c.flags & kFlagCommit) != 0;
   const __amdgpu_buffer_rsrc_t rec =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
-  SeqState pre;
-  const bool do_commit = (c.flags & kFlagCommit) != 0;
-  if (do_commit && wave == 0) pre = load_seq_state(c, b);
-  // records [G][nrows_total] (the GEMM kernels write each workgroup's records as one run): a
-  // load instruction of the merge reads 16-byte records of 4 consecutive rows per record index
-  finalize_sequences<false, false>(c, rec, G, 1, nrows_total, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  const int r = part * kFinRows + wave * 4 + (lane >> 4);   // row within the sequence
+  const bool rin = r < c.L;
+  const int row = b * c.L + (rin ? r : 0);
+  const int j = lane & 15;
+  Stats t;
+  if (G <= kGroup) {
+    const float4 v = record_load_after_kernel(rec, j < G && rin ? 16u * (unsigned)(row + j * nrows_total) : kOOB);
+    t = stats_row16_merge(stats_unpack(j < G ? v : stats_pack(stats_empty())));
+  } else {
+    float4 v[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) {
+      const int g = kGroup * j + k;
+      v[k] = record_load_after_kernel(rec, g < G && rin ? 16u * (unsigned)(row + g * nrows_total) : kOOB);
+    }
+    Stats q[kGroup];
+#pragma unroll
+    for (int k = 0; k < kGroup; ++k) q[k] = kGroup * j + k < G ? stats_unpack(v[k]) : stats_empty();
+    t = stats_row16_merge(stats_tree(q));
+  }
+  // S >= 1 in exact arithmetic; the rounding of m*log2(e) may put 1/S a few ulps above 1
+  const float conf = fminf(1.f / t.s, 1.f), gap = t.m1 - t.m2;
+  if (!do_commit) {
+    if (rin && j == 0) {
+      if (c.out_records) {                                // vocabulary shard: the merged record
+        Stats o = t;
+        o.id = t.id + c.v_begin;
+        c.out_records[row] = stats_pack(o);
+      } else {
+        c.out_tokens[row] = t.id;
+        if (c.out_conf) c.out_conf[row] = conf;
+        if (c.out_gap) c.out_gap[row] = gap;
+      }
+    }
+    return;
+  }
+  const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(row_out, 0, c.B * c.L * 16, 0x00020000);
+  if (rin && j == 0) record_store(out, 16u * (unsigned)row, make_float4(conf, __int_as_float(t.id), gap, 0.f));
+  __builtin_amdgcn_s_waitcnt(0);                          // published before this part is counted
+  __syncthreads();
+  __shared__ int s_last;
+  if (tid == 0) {
+    const unsigned prev = __builtin_amdgcn_atomic_inc32(tickets + b, (unsigned)(parts - 1), __ATOMIC_RELAXED, "agent");
+    s_last = prev == (unsigned)(parts - 1);
+  }
+  SeqState pre;                                           // (used by the last part only)
+  if (wave == 0) pre = load_seq_state(c, b);
+  __syncthreads();
+  if (!s_last || wave != 0) return;
+  const bool in = lane < c.L;
+  const float4 v = record_load(out, in ? 16u * (unsigned)(b * c.L + lane) : kOOB);
+  commit_sequence(c, b, in ? v.x : 0.f, in ? __float_as_int(v.y) : 0, pre);
+  if (in) {
+    if (c.out_conf) c.out_conf[b * c.L + lane] = v.x;
+    if (c.out_gap) c.out_gap[b * c.L + lane] = v.z;
+  }
 }
 
 // Top-k export of one row (one wavefront).  Lane l holds the row's best-first lists g = l, l + 64,
@@ -1484,7 +1548,7 @@ __device__ __forceinline__ void topk_merge_row(const CommitArgs& c, TopK (&t)[N]
 }
 
 // Merge + commit after the streaming kernel with the top-k fold.  Workgroups [0, B) merge and
-// commit one sequence each, as finalize_kernel; the others take one row per wavefront: they merge
+// commit one sequence each (finalize_sequences); the others take one row per wavefront: they merge
 // its statistics records again (same order, same result) for M and S, then its top-k records.
 // Every load of a row is issued before the first wait (records past G read as out of range and
 // are replaced by empty values), so a row costs one round trip to memory.

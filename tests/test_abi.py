@@ -63,14 +63,18 @@ def test_workspace_sizes():
     assert nat.dlm_workspace_bytes(1, 64, 2048, 126464, nat.DLM_BF16) == 256 + 64 * 256 * 16 + 64 * 16 * 16
     assert nat.dlm_workspace_bytes(1, 8, 64, 1024, nat.DLM_F32) == 256 + 16 * 64 * 16 + 16 * 4 * 16  # 64 tiles
     # GEMM-shaped path (bf16, more than 64 rows): records for every (padded row, workgroup of its
-    # row group), then the hidden rows in fragment order (rows padded to 32); up to 256 rows one
-    # 256-row group against 256-row vocabulary tiles, beyond that 512-row groups against 128-row
-    # tiles; workgroups per group a multiple of 8 where there are enough tiles
-    assert nat.dlm_workspace_bytes(8, 32, 2048, 157184, nat.DLM_BF16) == 256 + 256 * 256 * 16 + 256 * 2048 * 2
+    # row group), then the hidden rows in fragment order (rows padded to 32), then one 16-byte
+    # value per row for the commit; a counter per sequence first (padded to 256 B); up to 256 rows
+    # one 256-row group against 256-row vocabulary tiles, beyond that 512-row groups against
+    # 128-row tiles; workgroups per group a multiple of 8 where there are enough tiles
+    assert nat.dlm_workspace_bytes(8, 32, 2048, 157184, nat.DLM_BF16) == \
+        256 + 256 * 256 * 16 + 256 * 2048 * 2 + 256 * 16
     assert nat.dlm_workspace_bytes(16, 32, 2048, 157184, nat.DLM_BF16) == \
-        256 + 512 * 256 * 16 + 512 * 2048 * 2   # 1228 tiles, one group of 256 workgroups
+        256 + 512 * 256 * 16 + 512 * 2048 * 2 + 512 * 16   # 1228 tiles, one group of 256 workgroups
     assert nat.dlm_workspace_bytes(17, 31, 512, 5003, nat.DLM_BF16) == \
-        256 + 1024 * 40 * 16 + 544 * 512 * 2   # 40 tiles, 2 groups, 527 rows padded to 544
+        256 + 1024 * 40 * 16 + 544 * 512 * 2 + 527 * 16   # 40 tiles, 2 groups, 527 rows padded to 544
+    assert nat.dlm_workspace_bytes(128, 8, 256, 5003, nat.DLM_BF16) == \
+        512 + 1024 * 40 * 16 + 1024 * 256 * 2 + 1024 * 16   # 128 counters: 512 B
     for bad in [(0, 8, 64, 64, 0), (1, 65, 64, 64, 0), (1, 8, 48, 64, 0), (1, 8, 64, 0, 0), (1, 8, 64, 64, 5),
                 (257, 8, 64, 64, 1), (1, 8, 1 << 20, 64, 1), (1, 8, 4128, 64, 1), (1, 8, 2080, 64, 0)]:
         assert nat.dlm_workspace_bytes(*bad) == 0, bad
