@@ -165,7 +165,8 @@ typedef struct {
  *   out_tokens   [B][L]      int32    candidate (arg-max token) of EVERY row
  *   out_commit   [B][L]      uint8    1 where this call fixed the position
  * Every row goes through the LM head; the [B][L][V] logits never reach memory.
- * The workspace carries a completion counter that each call leaves at zero.
+ * The workspace carries completion counters (one per call, or one per sequence beyond 64 rows)
+ * that each call leaves at zero.
  * hidden and W_vocab must be finite: the kernels are built without NaN handling, so
  * NaN or Inf inputs give unspecified (but in-bounds, non-faulting) results.
  */
