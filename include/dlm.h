@@ -114,7 +114,9 @@ typedef struct {
   uint32_t flags;            /* DLM_AUTO_ADVANCE                                           */
   const dlm_seq_policy* seq; /* HOST array [B]; at most DLM_MAX_RULES distinct entries     */
   void* workspace;           /* device scratch, >= dlm_workspace_bytes(B, L, H, V, dtype)   */
-  size_t workspace_bytes;    /* its size; must be zero-filled before its first use         */
+  size_t workspace_bytes;    /* its size; must be zero-filled before its first use, and
+                                serves calls of one shape (B, L, H, V, dtype, topk): another
+                                shape needs its own workspace or a dlm_workspace_init first  */
   void* stream;              /* hipStream_t                                                */
   float* out_conf;           /* optional device [B][L]: confidence of every row, or NULL   */
   float* out_gap;            /* optional device [B][L]: top-1 minus top-2 logit, or NULL   */
