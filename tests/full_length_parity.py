@@ -1,6 +1,7 @@
 """Full-length lockstep parity on the GPU: each workload for its whole run, not a prefix.
 
-Not collected by pytest (a few minutes of oracle time); run it by name on a GPU machine:
+tests/test_gpu_full_runs.py runs it for every workload in the GPU suite; it also runs by name on
+a GPU machine:
 
     python tests/full_length_parity.py [workload ...]
 
