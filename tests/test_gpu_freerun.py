@@ -26,12 +26,12 @@ def gpu():
     _native.load()
 
 
-@pytest.mark.parametrize("name,steps,sample", [
-    ("tiny_threshold_f32", 24, [0]),
-    ("threshold_b1_l32", 24, [0]),
-    ("credit_b1_l32", 24, [0]),
-    ("hierarchical_b1_l64", 16, [0]),
-    ("mixed_b16_l32", 6, [0, 9]),
+@pytest.mark.parametrize("name,steps,sample", [   # each workload's whole run (a margin past it at B=1)
+    ("tiny_threshold_f32", 24, [0]),             # three blocks
+    ("threshold_b1_l32", 120, [0]),              # 32 blocks take ~108 steps
+    ("credit_b1_l32", 120, [0]),                 # ~107
+    ("hierarchical_b1_l64", 190, [0]),           # ~180
+    ("mixed_b16_l32", 64, [0, 7, 8, 15]),        # the workload's 64 steps; threshold 0, 7, credit 8, 15
 ])
 def test_free_running(name, steps, sample):
     from decoding_step_amd import _native as nat
