@@ -253,6 +253,9 @@ def cpu_baseline(wl, W, budget_s=20.0, topk=0):
     from threadpoolctl import threadpool_info, threadpool_limits
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
     seq = [(p.kind, p.threshold, p.decay, p.max_depth) for p in wl.policies]
+    # the oracle's exact float64 values of W, widened once before any timing (as the parity tests
+    # do): a weight conversion per step would be timed as oracle work
+    W64 = oracle.as_f64(W)
     streams = [BlockStream(W, wl.L, s, wl.a_max, rp) for s, rp in zip(wl.seeds, wl.redraw_p)]
     mask = np.ones((wl.B, wl.L), np.uint8)
     ctok = np.full((wl.B, wl.L, 4), -1, np.int32)
@@ -262,9 +265,9 @@ def cpu_baseline(wl, W, budget_s=20.0, topk=0):
     while t < budget_s and n < 64:
         h = np.stack([streams[b].hidden(*pos[b]) for b in range(wl.B)])
         t0 = time.perf_counter()
-        out = oracle.decode_step(h, W, mask, seq, ctok, cval, auto_advance=True)
+        out = oracle.decode_step(h, W64, mask, seq, ctok, cval, auto_advance=True)
         if topk:
-            oracle.topk_candidates(h, W, topk)
+            oracle.topk_candidates(h, W64, topk)
         t += time.perf_counter() - t0
         mask, ctok, cval = out["mask"], out["credit_tok"], out["credit_val"]
         for b in range(wl.B):
@@ -274,10 +277,10 @@ def cpu_baseline(wl, W, budget_s=20.0, topk=0):
     h = np.stack([BlockStream(W, wl.L, sd, wl.a_max, rp).hidden(0, 0) for sd, rp in zip(wl.seeds, wl.redraw_p)])
     with threadpool_limits(limits=1, user_api="blas"):
         t1 = time.perf_counter()
-        oracle.decode_step(h, W, np.ones((wl.B, wl.L), np.uint8), seq, np.full((wl.B, wl.L, 4), -1, np.int32),
+        oracle.decode_step(h, W64, np.ones((wl.B, wl.L), np.uint8), seq, np.full((wl.B, wl.L, 4), -1, np.int32),
                            np.zeros((wl.B, wl.L, 4), np.float32), auto_advance=True)
         if topk:
-            oracle.topk_candidates(h, W, topk)
+            oracle.topk_candidates(h, W64, topk)
         t1 = time.perf_counter() - t1
     model = ""
     try:
@@ -286,7 +289,8 @@ def cpu_baseline(wl, W, budget_s=20.0, topk=0):
     except OSError:  # pragma: no cover
         pass
     return {"value": wl.B * wl.L * n / t, "unit": "positions/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {n} steps of {wl.name} (whole steps, all {wl.B * wl.L} rows), {t:.1f} s",
+            "sample": f"first {n} steps of {wl.name} (whole steps, all {wl.B * wl.L} rows), {t:.1f} s; "
+                      f"W widened to float64 once, before the timed steps",
             "one_thread_value": wl.B * wl.L / t1, "affinity_cpus": len(os.sched_getaffinity(0)), "cpu_model": model}
 
 

@@ -2,8 +2,9 @@
 
 The counters are read in their own profiler runs, one counter per run, as CSV
 (``rocprofv3 --pmc FETCH_SIZE --output-format csv -d DIR -o run -- ...``).  A plain
-device-to-device copy of a known size (``copy_probe.py``) run the same way gives the
-factor between each counter's units and bytes.  The result is written as JSON next to
+device-to-device copy of a known size (512 MiB, ``torch`` ``copy_`` between two device
+buffers, run inline with ``python3 -c``) profiled the same way gives the factor between each
+counter's units and bytes.  The result is written as JSON next to
 the summaries under ``profiles/``, tagged with a hash of the kernel sources and build
 flags; ``bench.py`` reports it as ``roofline.traffic`` only while that hash matches.
 

@@ -11,9 +11,22 @@ itself says the decision is a near-tie:
 * F3 -- a forced pick whose best two candidates are within 1e-3.
 
 A sequence with an F2/F3 flag (or an F1 flag under credit decoding) is
-exempt as a whole for that step; flags are counted and reported.
-Confidences must agree to 1e-3 relative everywhere, credit values to 1e-3
-relative / 1e-6 absolute where not exempt.
+exempt from the comparison with the oracle's commits for that step; flags
+are counted and reported.  Confidences must agree to 1e-3 relative
+everywhere, credit values to 1e-3 relative / 1e-6 absolute where not exempt.
+
+Exempt is not unchecked.  Where several answers are correct the GPU's must
+be one of them:
+
+* a row with a near-tie (F1) must carry a near-maximal token: the oracle's
+  own logit of the GPU's token, rounded to float32, at least the row's top
+  logit minus 1e-2 (:func:`check_near_max_tokens`);
+* on EVERY followed sequence, flagged or not, the oracle's policy applied to
+  the GPU's own confidences and candidates must reproduce the GPU's commits,
+  mask and credit slots bit for bit (:func:`check_policy_replay`).  So each
+  commit passes its rule on the GPU's values, or is the rule's forced pick;
+  commits lie inside the mask; at least one commit is made while a position is
+  masked; and the credit update is the rule's.
 """
 from __future__ import annotations
 
@@ -73,6 +86,45 @@ def sequence_flags(kind, thr, mask_in, ref_b, advance):
     return flags
 
 
+def check_near_max_tokens(h_rows, W64, gpu_tok, ref_tok, ref_gap, label):
+    """Rows with a near-tie in the oracle (top-2 gap < 1e-2): the GPU's token must be a valid
+    arg-max within the flag tolerance, i.e. its float32-rounded oracle logit is at least the
+    row's top logit minus 1e-2.  Returns the number of such rows."""
+    rows = np.nonzero(np.asarray(ref_gap) < GAP_FLAG)[0]
+    V = W64.shape[0]
+    for r in rows:
+        g = int(gpu_tok[r])
+        assert 0 <= g < V, f"{label}: row {r}: token {g} outside the vocabulary"
+        h = oracle.as_f64(h_rows[r])
+        zg = np.float32(h @ W64[g])
+        zt = np.float32(h @ W64[int(ref_tok[r])])
+        assert zg >= zt - np.float32(GAP_FLAG), (
+            f"{label}: row {r}: GPU token {g} has logit {zg}, the top ({int(ref_tok[r])}) {zt}")
+    return len(rows)
+
+
+def check_policy_replay(rule, mask_in, ctok_in, cval_in, g, b, advance, label):
+    """The oracle's commit policy run on the GPU's own confidences and candidates of sequence b
+    (``g``: the GPU's outputs and state after the step) must give the GPU's commits, mask and
+    credit slots bit for bit; the commits must lie inside the (possibly refilled) mask, with at
+    least one while any position is masked."""
+    L = len(mask_in)
+    conf = np.asarray(g["conf"][b], np.float32)
+    tok = np.asarray(g["tokens"][b], np.int64)
+    rep = oracle.decode_step(np.zeros((1, L, 1), np.float32), np.zeros((1, 1), np.float32), mask_in[None], [rule],
+                             ctok_in[None], cval_in[None], auto_advance=advance,
+                             stats={"conf": conf[None], "tok": tok[None], "gap": np.ones((1, L), np.float32)})
+    np.testing.assert_array_equal(g["commit"][b], rep["commit"][0], err_msg=f"{label}: commits vs the rule")
+    np.testing.assert_array_equal(g["mask"][b], rep["mask"][0], err_msg=f"{label}: mask vs the rule")
+    if rule[0] == CREDIT:
+        np.testing.assert_array_equal(g["ctok"][b], rep["credit_tok"][0], err_msg=f"{label}: credit slots vs the rule")
+        np.testing.assert_array_equal(g["cval"][b], rep["credit_val"][0], err_msg=f"{label}: credit values vs the rule")
+    eff = np.ones(L, bool) if (advance and not mask_in.any()) else mask_in.astype(bool)
+    com = np.asarray(g["commit"][b]).astype(bool)
+    assert not (com & ~eff).any(), f"{label}: a commit outside the mask"
+    assert com.any() == eff.any(), f"{label}: no commit while positions are masked"
+
+
 class Lockstep:
     """Drive a workload through both paths, comparing every step."""
 
@@ -90,6 +142,7 @@ class Lockstep:
         self.sample = list(range(self.B)) if sample_seqs is None else list(sample_seqs)
         self.flags = Counter()
         self.checked = Counter()
+        self.exempt = Counter()
         self.commits = 0
         self.steps = 0
 
@@ -117,16 +170,23 @@ class Lockstep:
             fl = sequence_flags(kind, thr, self.mask[b], ref_b, True)
             for f in fl:
                 self.flags[f] += 1
+            label = f"seq {b}, step {self.steps}"
             tok_ok = ref["gap"][i] >= GAP_FLAG
             np.testing.assert_array_equal(g["tokens"][b][tok_ok], ref["tokens"][i][tok_ok],
-                                          err_msg=f"tokens, seq {b}, step {self.steps}")
+                                          err_msg=f"tokens, {label}")
+            self.exempt["near-tie rows (token near-maximal)"] += check_near_max_tokens(
+                h[b], self.W64, g["tokens"][b], ref["tokens"][i], ref["gap"][i], label)
+            check_policy_replay(self.seq[b], self.mask[b], self.ctok[b], self.cval[b], g, b, True, label)
+            self.checked["rule replays"] += 1
             np.testing.assert_allclose(g["conf"][b], ref["conf"][i], rtol=CONF_RTOL,
                                        err_msg=f"conf, seq {b}, step {self.steps}")
             finite = np.isfinite(ref["gap"][i])
             np.testing.assert_allclose(g["gap"][b][finite], ref["gap"][i][finite], rtol=1e-3, atol=2e-3,
                                        err_msg=f"gap, seq {b}, step {self.steps}")
             exempt = bool(fl & {"F2", "F3"}) or (kind == CREDIT and "F1" in fl)
-            if not exempt:
+            if exempt:
+                self.exempt["sequence-steps (valid by the rule replay)"] += 1
+            else:
                 self.checked["sequences"] += 1
                 np.testing.assert_array_equal(g["commit"][b], ref["commit"][i],
                                               err_msg=f"commit, seq {b}, step {self.steps}")
@@ -158,6 +218,6 @@ class Lockstep:
             if blocks is not None and min(p[0] for p in self.pos) >= blocks:
                 break
             self.step()
-        say(f"[{label}] {self.steps} steps, {self.commits} commits (sampled), flags {dict(self.flags)}, "
-            f"checked {dict(self.checked)}, {time.time() - t0:.1f}s")
+        say(f"[{label}] {self.steps} steps, {self.commits} commits (followed sequences), flags {dict(self.flags)}, "
+            f"checked {dict(self.checked)}, exempt {dict(self.exempt)}, {time.time() - t0:.1f}s")
         return self

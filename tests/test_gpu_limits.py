@@ -9,7 +9,7 @@ import numpy as np
 import pytest
 
 import oracle
-from parity_util import GAP_FLAG, sequence_flags, say
+from parity_util import GAP_FLAG, check_near_max_tokens, check_policy_replay, sequence_flags, say
 
 torch = pytest.importorskip("torch")
 
@@ -61,6 +61,7 @@ def test_token_stats_at_the_limits(B, L, H, V):
     conf, tok, gap = conf.cpu().numpy()[rows], tok.cpu().numpy()[rows], gap.cpu().numpy()[rows]
     sure = ref["gap"] >= 1e-2
     np.testing.assert_array_equal(tok[sure], ref["tok"][sure])
+    check_near_max_tokens(h[rows], oracle.as_f64(W), tok, ref["tok"], ref["gap"], f"B={B} L={L} H={H} V={V}")
     np.testing.assert_allclose(conf, ref["conf"], rtol=1e-3)
     fin = np.isfinite(ref["gap"])
     np.testing.assert_allclose(gap[fin], ref["gap"][fin], rtol=1e-3, atol=2e-3)
@@ -75,7 +76,7 @@ def test_largest_block_batch_whole_step():
     """One full step at B=256, L=64 (threshold and credit rules), commits checked on sampled
     sequences against the oracle from the same state."""
     from decoding_step_amd import _native as nat
-    from decoding_step_amd.device import Decoder, credit_tokens, new_credit, to_device
+    from decoding_step_amd.device import Decoder, credit_tokens, credit_values, new_credit, to_device
     from decoding_step_amd.synth import BlockStream, make_weights
     B, L, H, V = 256, 64, 1024, 12007
     say(f"gpu: whole step at B={B} L={L}")
@@ -88,16 +89,22 @@ def test_largest_block_batch_whole_step():
     dec.step(to_device(h), mask, credit)
     torch.cuda.synchronize()
     sample = [0, 1, 127, 128, 254, 255]
-    ref = oracle.decode_step(h[sample], oracle.as_f64(W), np.ones((len(sample), L), np.uint8),
+    W64 = oracle.as_f64(W)
+    ref = oracle.decode_step(h[sample], W64, np.ones((len(sample), L), np.uint8),
                              [seq[b] for b in sample], auto_advance=True)
     g_com, g_mask = dec.out_commit.cpu().numpy(), mask.cpu().numpy()
     g_tok, g_ctok = dec.out_tokens.cpu().numpy(), credit_tokens(credit).cpu().numpy()
+    g = {"conf": dec.conf.cpu().numpy(), "tokens": g_tok, "commit": g_com, "mask": g_mask, "ctok": g_ctok,
+         "cval": credit_values(credit).cpu().numpy()}
     compared = 0
     for i, b in enumerate(sample):
         ref_b = {k: ref[k][i] for k in ("conf", "score", "gap", "commit")}
         fl = sequence_flags(seq[b][0], seq[b][1], np.ones(L, np.uint8), ref_b, True)
         sure = ref["gap"][i] >= GAP_FLAG
         np.testing.assert_array_equal(g_tok[b][sure], ref["tokens"][i][sure], err_msg=f"tokens seq {b}")
+        check_near_max_tokens(h[b], W64, g_tok[b], ref["tokens"][i], ref["gap"][i], f"seq {b}")
+        check_policy_replay(seq[b], np.ones(L, np.uint8), np.full((L, 4), -1, np.int32), np.zeros((L, 4), np.float32),
+                            g, b, True, f"seq {b}")
         if fl & {"F2", "F3"} or (seq[b][0] == oracle.CREDIT and "F1" in fl):
             continue
         compared += 1
