@@ -54,6 +54,11 @@ def test_free_running(name, steps, sample):
     o_cval = {b: np.zeros((L, 4), np.float32) for b in sample}
     following, diverged = set(sample), []
     compared = commits = near_ties = 0
+    # the GPU's own state before each step (the rule replay starts from it: in free running the GPU's
+    # credit values may differ from the oracle's in the last bits while everything else agrees)
+    p_mask = np.ones((B, L), np.uint8)
+    p_ctok = np.full((B, L, 4), -1, np.int32)
+    p_cval = np.zeros((B, L, 4), np.float32)
     for n in range(steps):
         h = np.stack([streams[b].hidden(*pos[b]) for b in range(B)])
         dec.step(to_device(h), mask, credit)
@@ -79,7 +84,7 @@ def test_free_running(name, steps, sample):
                 # and its commits / mask / credit are its rule applied to its own values
                 near_ties += check_near_max_tokens(h[b], W64, g_tok[b], ref["tokens"][i], ref["gap"][i],
                                                    f"seq {b} step {n}")
-                check_policy_replay(seq[b], o_mask[b], o_ctok[b], o_cval[b], g, b, True, f"seq {b} step {n}")
+                check_policy_replay(seq[b], p_mask[b], p_ctok[b], p_cval[b], g, b, True, f"seq {b} step {n}")
                 same = (np.array_equal(g_com[b], ref["commit"][i]) and np.array_equal(g_mask[b], ref["mask"][i])
                         and np.array_equal(g_ctok[b], ref["credit_tok"][i]))
                 if same and seq[b][0] == oracle.CREDIT:
@@ -92,6 +97,7 @@ def test_free_running(name, steps, sample):
                     assert flagged, f"sequence {b} diverged at step {n} with no near-tie flag ({sorted(fl)})"
                     diverged.append((b, n, sorted(fl)))
                     following.discard(b)
+        p_mask, p_ctok, p_cval = g_mask.copy(), g_ctok.copy(), g_cval.copy()
         for b in range(B):
             pos[b] = [pos[b][0] + 1, 0] if not g_mask[b].any() else [pos[b][0], pos[b][1] + 1]
     say(f"[{name}] free-running: {compared} sequence-steps equal, {commits} commits, "
