@@ -22,6 +22,7 @@ DLM_THRESHOLD, DLM_HIERARCHICAL, DLM_CREDIT = 0, 1, 2
 DLM_AUTO_ADVANCE = 1
 DLM_SEQ_RUNNING, DLM_SEQ_FINISHED, DLM_SEQ_EOS_IN_BLOCK = 0, 1, 2
 DLM_MAX_SEQS, DLM_MAX_L, DLM_CREDIT_SLOTS, DLM_MAX_RULES, DLM_MAX_TOPK, DLM_MAX_SHARDS = 256, 64, 4, 8, 8, 256
+DLM_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 STATUS_NAMES = {0: "DLM_OK", -1: "DLM_ERR_NULL", -2: "DLM_ERR_DTYPE", -3: "DLM_ERR_SHAPE",
                 -4: "DLM_ERR_POLICY", -5: "DLM_ERR_WORKSPACE", -6: "DLM_ERR_HIP"}
@@ -74,6 +75,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     pol = ctypes.POINTER(dlm_policy)
     lib.dlm_decode_step.argtypes = [vp, vp, vp, vp, pol, vp, vp]
     lib.dlm_decode_step.restype = ctypes.c_int
+    lib.dlm_decode_step_noalloc.argtypes = [vp, vp, vp, vp, pol, vp, vp]
+    lib.dlm_decode_step_noalloc.restype = ctypes.c_int
     lib.dlm_decode_steps.argtypes = [vp, vp, vp, vp, pol, i64, vp, vp]
     lib.dlm_decode_steps.restype = ctypes.c_int
     lib.dlm_token_stats.argtypes = [vp, vp, pol, vp, vp, vp]
@@ -189,6 +192,13 @@ class StepPolicy:
 def dlm_decode_step(hidden, W_vocab, mask_state, credit_state, policy: StepPolicy, out_tokens, out_commit) -> None:
     _check(load().dlm_decode_step(_ptr(hidden), _ptr(W_vocab), _ptr(mask_state), _ptr(credit_state),
                                   ctypes.byref(policy.c), _ptr(out_tokens), _ptr(out_commit)))
+
+
+def dlm_decode_step_noalloc(hidden, W_vocab, mask_state, credit_state, policy: StepPolicy, out_tokens,
+                            out_commit) -> None:
+    """dlm_decode_step with the library's static per-GPU scratch as workspace (policy's workspace ignored)."""
+    _check(load().dlm_decode_step_noalloc(_ptr(hidden), _ptr(W_vocab), _ptr(mask_state), _ptr(credit_state),
+                                          ctypes.byref(policy.c), _ptr(out_tokens), _ptr(out_commit)))
 
 
 def dlm_decode_steps(hidden_steps, W_vocab, mask_state, credit_state, policy: StepPolicy, n_steps: int,

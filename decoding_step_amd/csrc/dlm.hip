@@ -8,6 +8,7 @@
 #include <cstring>
 #include <string>
 #include <algorithm>
+#include <mutex>
 
 #include "dlm.h"
 #include "dlm_device.hpp"
@@ -61,7 +62,11 @@ int elem_bytes(int32_t dtype) { return dtype == DLM_BF16 ? 2 : dtype == DLM_F32 
 
 // topk > 0 selects the streaming kernel with the top-k fold for every shape (the GEMM-shaped head
 // has none) and appends its records to the workspace; the caller validates topk's range.
-int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int topk, Plan* p) {
+// fixed_ticket_bytes > 0 places the counters in a region of that size at the start of the
+// workspace whatever the shapes (the records follow it), so that calls of different shapes
+// sharing one workspace never find another shape's records where their counters are.
+int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int topk, Plan* p,
+              size_t fixed_ticket_bytes = 0) {
   const int es = elem_bytes(dtype);
   if (!es) return fail(DLM_ERR_DTYPE, "dtype %d is neither DLM_F32 (0) nor DLM_BF16 (1)", (int)dtype);
   if (B < 1 || B > DLM_MAX_SEQS) return fail(DLM_ERR_SHAPE, "B=%lld outside [1, %d]", (long long)B, DLM_MAX_SEQS);
@@ -95,6 +100,10 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
     // per-sequence counters [B] (padded to 256 bytes) | records [G_t][n_rg * rows] | hidden rows
     // in fragment order, padded to 32 rows | published per-row values [B*L] x 16 bytes
     p->ticket_bytes = (size_t)((4 * B + 255) / 256 * 256);
+    if (fixed_ticket_bytes) {
+      if (p->ticket_bytes > fixed_ticket_bytes) return fail(DLM_ERR_SHAPE, "B=%lld: too many counters", (long long)B);
+      p->ticket_bytes = fixed_ticket_bytes;
+    }
     p->packed_off = p->ticket_bytes + (size_t)n_rg * rows * G_t * 16;
     p->packed_bytes = (size_t)m_pad * H * 2;
     p->rowout_off = p->packed_off + p->packed_bytes;
@@ -133,6 +142,10 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
   const int64_t nq = (G_v + dlm::kGroup - 1) / dlm::kGroup;
   p->nq = (int)nq;
   p->ticket_bytes = (size_t)((4 * (1 + n_rg * nq) + 255) / 256 * 256);
+  if (fixed_ticket_bytes) {
+    if (p->ticket_bytes > fixed_ticket_bytes) return fail(DLM_ERR_SHAPE, "B*L=%lld: too many counters", (long long)M);
+    p->ticket_bytes = fixed_ticket_bytes;
+  }
   p->level2_off = p->ticket_bytes + (size_t)n_rg * MR * G_v * 16;
   p->ws = p->level2_off + (size_t)n_rg * MR * nq * 16;
   if (topk) {
@@ -235,9 +248,9 @@ int head_event(const dlm_policy* pol, bool time_head, int i, hipStream_t stream)
 }
 
 int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::CommitArgs c, bool commit,
-             bool time_head) {
+             bool time_head, size_t fixed_ticket_bytes = 0) {
   Plan p;
-  int rc = make_plan(pol->B, pol->L, pol->H, pol->V, pol->dtype, c.topk, &p);
+  int rc = make_plan(pol->B, pol->L, pol->H, pol->V, pol->dtype, c.topk, &p, fixed_ticket_bytes);
   if (rc) return rc;
   if (!pol->workspace) return fail(DLM_ERR_NULL, "policy->workspace is NULL");
   if (pol->workspace_bytes < p.ws)
@@ -323,6 +336,49 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   return head_event(pol, time_head, 1, stream);
 }
 
+// ---- the workspace of dlm_decode_step_noalloc --------------------------------------------------
+// One static array per GPU the library runs on (each device holds its own copy of it until the
+// process ends).  In host code `scratch` names a host-side stand-in, not the device memory: host
+// code uses only the per-device address that hipGetSymbolAddress returns.
+constexpr size_t kScratchBytes = DLM_NOALLOC_SCRATCH_BYTES;
+// Counter region at the start of the array, large enough for every shape that fits the array
+// (at most 4 * (1 + 1024) bytes on the streaming path, 4 * DLM_MAX_SEQS on the GEMM-shaped one).
+constexpr size_t kScratchTicketBytes = 8192;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[DLM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// This device's copy of `scratch`.  On the first call on a device: its address, then a fill
+// kernel on `stream` that zeroes the counter region (the counters must start at zero; every call
+// leaves them at zero again).  The records and staging areas need no clearing.
+int scratch_of_current_device(hipStream_t stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(DLM_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(DLM_ERR_HIP, "device %d: at most %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) return fail(DLM_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    const int blocks = (int)((kScratchTicketBytes / 16 + 255) / 256);
+    hipLaunchKernelGGL(dlm::fill_zero_kernel, dim3(blocks), dim3(256), 0, stream, static_cast<uint8_t*>(ptr),
+                       kScratchTicketBytes, blocks * 256);
+    e = hipGetLastError();
+    if (e != hipSuccess) return fail(DLM_ERR_HIP, "scratch counter clear: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,6 +404,42 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
   c.out_conf = policy->out_conf;
   c.out_gap = policy->out_gap;
   return run_step(hidden, W_vocab, policy, c, true, true);
+}
+
+int dlm_decode_step_noalloc(const void* hidden, const void* W_vocab, uint8_t* mask_state,
+                            dlm_credit_slot* credit_state, const dlm_policy* policy, int32_t* out_tokens,
+                            uint8_t* out_commit) {
+  if (!policy) return fail(DLM_ERR_NULL, "policy is NULL");
+  if (!hidden || !W_vocab || !mask_state || !out_tokens || !out_commit)
+    return fail(DLM_ERR_NULL, "hidden, W_vocab, mask_state, out_tokens and out_commit must be non-NULL");
+  dlm::CommitArgs c;
+  std::memset(&c, 0, sizeof c);
+  int rc = check_topk(policy, &c);
+  if (rc) return rc;
+  Plan p;
+  rc = make_plan(policy->B, policy->L, policy->H, policy->V, policy->dtype, c.topk, &p, kScratchTicketBytes);
+  if (rc) return rc;
+  if (p.ws > kScratchBytes)
+    return fail(DLM_ERR_WORKSPACE, "these shapes need %zu bytes of workspace; the static scratch of "
+                "dlm_decode_step_noalloc holds %zu (DLM_NOALLOC_SCRATCH_BYTES): use dlm_decode_step", p.ws,
+                kScratchBytes);
+  rc = pack_rules(policy, true, credit_state, policy->V, &c);
+  if (rc) return rc;
+  if (misaligned(hidden, 16) || misaligned(W_vocab, 16))   // (before the first call's clear is enqueued)
+    return fail(DLM_ERR_SHAPE, "hidden and W_vocab must be 16-byte aligned");
+  c.mask = mask_state;
+  c.credit = credit_state;
+  c.out_tokens = out_tokens;
+  c.out_commit = out_commit;
+  c.out_conf = policy->out_conf;
+  c.out_gap = policy->out_gap;
+  void* ws = nullptr;
+  rc = scratch_of_current_device(static_cast<hipStream_t>(policy->stream), &ws);
+  if (rc) return rc;
+  dlm_policy pol = *policy;
+  pol.workspace = ws;
+  pol.workspace_bytes = kScratchBytes;
+  return run_step(hidden, W_vocab, &pol, c, true, true, kScratchTicketBytes);
 }
 
 int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mask_state,

@@ -24,9 +24,10 @@
  *   - Arguments are validated on the host BEFORE any HIP call; on a non-zero
  *     status nothing is enqueued and nothing is written.  dlm_last_error()
  *     then returns a message (thread-local).
- *   - The library never allocates device memory in these calls and keeps no
- *     mutable global state; calls on different streams must use different
- *     workspaces.
+ *   - The library never allocates device memory in these calls.  Its only
+ *     mutable global state is the static scratch of dlm_decode_step_noalloc;
+ *     calls of the other entry points on different streams must use
+ *     different workspaces.
  */
 #ifndef DLM_H
 #define DLM_H
@@ -128,6 +129,7 @@ typedef struct {
   void* head_events[2];      /* optional hipEvent_t pair, each may be NULL (see below)      */
 } dlm_policy;
 
+
 /*
  * Timing the vocabulary head alone (dlm_decode_step and dlm_token_stats; the other calls ignore
  * the field).  head_events[0] is recorded on the stream right before the launch of the kernel
@@ -175,6 +177,31 @@ typedef struct {
 int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state,
                     dlm_credit_slot* credit_state, const dlm_policy* policy, int32_t* out_tokens,
                     uint8_t* out_commit);
+
+/*
+ * dlm_decode_step for callers that cannot allocate device memory (code being captured into a HIP
+ * graph, tight serving loops, harnesses that forbid hipMalloc): the same step, with the workspace
+ * taken from a static device array of DLM_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it runs on (until the process ends) instead of policy->workspace.  policy->workspace and
+ * workspace_bytes are ignored; every other argument and field means what it means for
+ * dlm_decode_step, and the results are the same bits.
+ *   - The array starts with a fixed 8 KB counter region; the rest of the workspace follows it.
+ *     Shapes that need more than DLM_NOALLOC_SCRATCH_BYTES in that layout (the workspace of
+ *     dlm_decode_step / dlm_workspace_bytes_topk plus at most 8 KB) give DLM_ERR_WORKSPACE
+ *     before anything is enqueued.  Blocks of up to 16 x 32 rows at V = 157184, H = 2048 fit
+ *     (about 3.2 MB), with or without the top-k export at one sequence.
+ *   - The call allocates and frees nothing.  The first call on a device looks up that device's
+ *     copy of the array and enqueues a fill kernel on `stream` that zeroes its counter region;
+ *     every call leaves the counters at zero again, so calls of different shapes may follow one
+ *     another freely.
+ *   - The current device (hipSetDevice) must be the device of `stream` and of the buffers.
+ *   - All calls on one GPU share its array: calls that overlap in time on one GPU (different
+ *     streams or threads without ordering between them) race and give wrong results.
+ */
+#define DLM_NOALLOC_SCRATCH_BYTES (8u << 20)
+int dlm_decode_step_noalloc(const void* hidden, const void* W_vocab, uint8_t* mask_state,
+                            dlm_credit_slot* credit_state, const dlm_policy* policy, int32_t* out_tokens,
+                            uint8_t* out_commit);
 
 /*
  * N decode steps enqueued back to back on policy->stream with no host work between them: the

@@ -46,6 +46,9 @@ def test_header_constants_match_binding():
     text = open(HEADER).read()
     for name in ["DLM_MAX_SEQS", "DLM_MAX_L", "DLM_CREDIT_SLOTS", "DLM_MAX_RULES", "DLM_MAX_TOPK", "DLM_MAX_SHARDS"]:
         assert int(re.search(rf"#define {name} (\d+)", text).group(1)) == getattr(nat, name)
+    assert int(re.search(r"#define DLM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).group(1)) << \
+        int(re.search(r"#define DLM_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text).group(2)) == \
+        nat.DLM_NOALLOC_SCRATCH_BYTES
     for name in ["DLM_SEQ_RUNNING", "DLM_SEQ_FINISHED", "DLM_SEQ_EOS_IN_BLOCK"]:
         assert int(re.search(rf"{name} = (\d+)", text).group(1)) == getattr(nat, name)
     assert ctypes.sizeof(nat.dlm_credit_slot) == 8
@@ -290,3 +293,30 @@ def test_binding_raises_without_library(tmp_path):
             nat.load(str(tmp_path / "missing.so"))
     finally:
         nat._lib = saved
+
+
+def noalloc_step(p, hidden=FAKE, W=FAKE, mask=FAKE, credit=FAKE, out_tok=FAKE, out_commit=FAKE):
+    return status_of(nat.dlm_decode_step_noalloc, hidden, W, mask, credit, p, out_tok, out_commit)
+
+
+def test_noalloc_validation():
+    # the same checks as dlm_decode_step, all before any HIP call; the policy's workspace is ignored
+    p = policy(ws=None, ws_bytes=0)
+    assert noalloc_step(p, hidden=None) == nat.DLM_ERR_NULL
+    assert noalloc_step(p, out_commit=None) == nat.DLM_ERR_NULL
+    assert nat.load().dlm_decode_step_noalloc(FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE) == nat.DLM_ERR_NULL
+    assert noalloc_step(policy(ws=None, dtype=2)) == nat.DLM_ERR_DTYPE
+    assert noalloc_step(policy(ws=None, L=65)) == nat.DLM_ERR_SHAPE
+    assert noalloc_step(policy(ws=None, seq=[(7, 0.9, 0.0, 0)])) == nat.DLM_ERR_POLICY
+    assert noalloc_step(policy(ws=None, seq=[(nat.DLM_CREDIT, 1.2, 0.7, 0)]), credit=None) == nat.DLM_ERR_NULL
+    # shapes beyond the static scratch: rejected with a clear message, nothing enqueued
+    big = dict(B=256, L=64, H=2048, V=157184)
+    assert nat.dlm_workspace_bytes(*big.values(), nat.DLM_BF16) > nat.DLM_NOALLOC_SCRATCH_BYTES
+    assert noalloc_step(policy(ws=None, seq=[(nat.DLM_THRESHOLD, 0.9, 0.0, 0)] * 256, **big)) == nat.DLM_ERR_WORKSPACE
+    assert "DLM_NOALLOC_SCRATCH_BYTES" in nat.dlm_last_error()
+    # the batched workload's shape, with and without the top-k export at one sequence, fits
+    # (the workspace plus the 8 KB counter region)
+    for B, L, H, V, k in [(16, 32, 2048, 157184, 0), (1, 32, 2048, 126464, 8), (1, 64, 2048, 126464, 8)]:
+        need = nat.dlm_workspace_bytes_topk(B, L, H, V, nat.DLM_BF16, k)
+        assert 0 < need and need - 256 + 8192 <= nat.DLM_NOALLOC_SCRATCH_BYTES, (B, L, k, need)
+    assert noalloc_step(policy(ws=None), hidden=MISALIGNED) == nat.DLM_ERR_SHAPE
