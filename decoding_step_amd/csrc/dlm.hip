@@ -51,8 +51,9 @@ struct Plan {
   size_t ws = 0;     // workspace bytes
   size_t packed_off = 0, packed_bytes = 0;  // GEMM path: fragment-ordered hidden rows in the workspace
   size_t rowout_off = 0;                    // GEMM path: published per-row conf / token / gap [B*L]
-  int topk = 0;      // streaming kernel with the top-k fold + finalize_topk_kernel
+  int topk = 0;      // streaming kernel with the top-k fold (merged with the statistics in-kernel)
   size_t topk_off = 0;                      // top-k records in the workspace
+  size_t topk_l2_off = 0;                   // second-level top-k records [rows][nq] x 64 bytes
   int nq = 0;        // streaming kernel: groups of dlm::kGroup vocabulary ranges (two-level merge)
   size_t ticket_bytes = kTicketBytes;       // completion counters: global, then [n_rg][nq] groups
   size_t level2_off = 0;                    // second-level records [n_rg * rows][nq]
@@ -149,11 +150,13 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
   p->level2_off = p->ticket_bytes + (size_t)n_rg * MR * G_v * 16;
   p->ws = p->level2_off + (size_t)n_rg * MR * nq * 16;
   if (topk) {
-    // ticket | records [n_rg * MR][G_v] | top-k records [n_rg * MR][G_v] x DLM_MAX_TOPK x 8 bytes
+    // ... | top-k lists [n_rg * MR][G_v] x DLM_MAX_TOPK x 8 bytes | second-level lists [n_rg * MR][nq] x 64
     if (n_rg * MR * G_v * (DLM_MAX_TOPK * 8) >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large for top-k");
     p->topk = 1;
     p->topk_off = p->ws;
     p->ws += (size_t)n_rg * MR * G_v * (DLM_MAX_TOPK * 8);
+    p->topk_l2_off = p->ws;
+    p->ws += (size_t)n_rg * MR * nq * (DLM_MAX_TOPK * 8);
     p->lds = dlm::lds_bytes_topk(NMB);
   }
   return DLM_OK;
@@ -272,6 +275,7 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   a.G_v = p.G_v;
   a.ntiles = p.ntiles;
   a.topk_records = p.topk ? reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.topk_off) : nullptr;
+  a.topk_level2 = p.topk ? reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.topk_l2_off) : nullptr;
   c.B = (int)pol->B;
   c.L = (int)pol->L;
   c.flags = (commit ? dlm::kFlagCommit : 0u) | (commit ? (pol->flags & DLM_AUTO_ADVANCE) : 0u);
@@ -316,22 +320,11 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "finalize kernel launch: %s", hipGetErrorString(e));
     return ok();
   }
-  if (p.topk) {
-    if ((rc = head_event(pol, time_head, 0, stream))) return rc;
-    rc = pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, true>(a, p, stream) : launch_step_for<float, true>(a, p, stream);
-    if (rc) return rc;
-    if ((rc = head_event(pol, time_head, 1, stream))) return rc;
-    const int rows = 16 * p.NMB;
-    const int M = a.M;
-    const int grid = c.B + (M + dlm::kWaves - 1) / dlm::kWaves;
-    hipLaunchKernelGGL(dlm::finalize_topk_kernel, dim3(grid), dim3(dlm::kThreads), 0, stream, a.c, a.partials,
-                       a.topk_records, p.G_v, p.n_rg * rows);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(DLM_ERR_HIP, "top-k finalize kernel launch: %s", hipGetErrorString(e));
-    return ok();
-  }
   if ((rc = head_event(pol, time_head, 0, stream))) return rc;
-  rc = pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, false>(a, p, stream) : launch_step_for<float, false>(a, p, stream);
+  if (p.topk)
+    rc = pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, true>(a, p, stream) : launch_step_for<float, true>(a, p, stream);
+  else
+    rc = pol->dtype == DLM_BF16 ? launch_step_for<uint16_t, false>(a, p, stream) : launch_step_for<float, false>(a, p, stream);
   if (rc) return rc;
   return head_event(pol, time_head, 1, stream);
 }

@@ -85,6 +85,7 @@ struct StepArgs {
   float4* topk_records;  // top-k fold only: [n_rg * 16 * NMB][G_v] lists of kTopK (logit, id)
   unsigned* group_tickets;  // [n_rg][nq] completion counters of the groups of kGroup ranges
   float4* level2;        // [n_rg * 16 * NMB][nq] merged record of each (row, group of ranges)
+  float4* topk_level2;   // top-k fold only: [n_rg * 16 * NMB][nq] merged lists of each (row, group)
   int nq;                // groups of ranges: ceil(G_v / kGroup)
   CommitArgs c;
 };
@@ -311,6 +312,42 @@ __device__ __forceinline__ void topk_row16_merge(TopK& t, TopK& out) {
   }
 }
 
+// A best-first list travels as four 16-byte records: (z0, id0, z1, id1), (z2, id2, z3, id3), ...
+__device__ __forceinline__ void topk_from_records(TopK& t, const float4 (&e)[kTopK / 2]) {
+#pragma unroll
+  for (int q = 0; q < kTopK / 2; ++q) {
+    t.z[2 * q] = e[q].x;
+    t.id[2 * q] = __float_as_int(e[q].y);
+    t.z[2 * q + 1] = e[q].z;
+    t.id[2 * q + 1] = __float_as_int(e[q].w);
+  }
+}
+
+__device__ __forceinline__ float4 topk_record(const TopK& t, int q) {
+  return make_float4(t.z[2 * q], __int_as_float(t.id[2 * q]), t.z[2 * q + 1], __int_as_float(t.id[2 * q + 1]));
+}
+
+// The export of one row from its merged list, which every lane of the row's 16-lane row holds:
+// lane j of that row writes rank j (readings T1-T3).  A rank's probability is
+// 2^((z - M) log2 e) / S with the row's maximum M and sum S, so rank 0 equals the confidence
+// min(1/S, 1) bit for bit; ranks past the vocabulary are token -1 with probability 0.
+__device__ __forceinline__ void topk_write_row(const CommitArgs& c, const TopK& best, int row, int j, float M,
+                                               float inv_s) {
+  float z = best.z[0];
+  int id = best.id[0];
+#pragma unroll
+  for (int i = 1; i < kTopK; ++i) {
+    z = j == i ? best.z[i] : z;
+    id = j == i ? best.id[i] : id;
+  }
+  if (j < c.topk) {
+    const bool real = id != kNoToken;
+    const size_t o = (size_t)row * c.topk + j;
+    c.out_topk_tokens[o] = real ? id : -1;
+    if (c.out_topk_prob) c.out_topk_prob[o] = real ? fminf(ex2((z - M) * kLog2e) * inv_s, 1.f) : 0.f;
+  }
+}
+
 // Statistics records are exchanged between workgroups with 16-byte buffer accesses carrying the
 // device-scope coherence bit (the cache policy the compiler gives device-scope atomics): stores
 // are written through to the device coherence point and loads read from it, so no cache
@@ -355,36 +392,14 @@ __device__ __forceinline__ void stats_fold1(Stats& st, float z, int v) {
   st.m1 = mnew;
 }
 
-// Merge the records of one row in a fixed two-level tree: the groups of kGroup consecutive
-// records first (a balanced binary tree over each group, in index order), then the group results,
-// in group order, as one more such tree.  The distributed merge at the end of step_kernel takes
-// the same two levels in separate workgroups (16-lane DPP trees), so every path that merges a
-// row's records produces the same bits.  Merging with an empty record gives the other operand
-// exactly, so records past G are empty ones and skipped work changes no bits.
-//
-// merge_records: one row per wavefront, lane l holding records 16*(l%16) + 4*(l/16) + i (i < 4):
-// the quarter of group l%16 in registers, the four quarters across rows (row swaps), the groups
-// across the 16 lanes of a row.  Every lane ends with the result.
-constexpr int kRecordsPerLane = kMaxVocabGroups / 64;
-static_assert(kRecordsPerLane == 4 && kGroup == 16, "a group is four quarters of four records");
-__device__ __forceinline__ int record_of_lane(int lane, int i) { return 16 * (lane & 15) + 4 * (lane >> 4) + i; }
-
-__device__ __forceinline__ Stats merge_records(const float4 (&r)[kRecordsPerLane], int G) {
-  Stats q[kRecordsPerLane];
-#pragma unroll
-  for (int i = 0; i < kRecordsPerLane; ++i) q[i] = stats_unpack(r[i]);
-  Stats t = stats_tree(q);
-  t = stats_merge_rows<16>(t);
-  t = stats_merge_rows<32>(t);            // group l%16 in every lane of column l%16
-  if (G > kGroup) return stats_row16_merge(t);
-  // one group (uniform branch): it is the result as it stands, in lane 0
-  Stats b;
-  b.m1 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.m1)));
-  b.s = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.s)));
-  b.m2 = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, t.m2)));
-  b.id = __builtin_amdgcn_readfirstlane(t.id);
-  return b;
-}
+// Every path that merges a row's per-range records follows one fixed two-level tree: the groups
+// of kGroup consecutive records first (a balanced binary tree over each group, in index order),
+// then the group results, in group order, as one more such tree.  The distributed merge at the
+// end of step_kernel takes the two levels in separate workgroups (16-lane DPP trees), the
+// finalizers in one (finalize_sequences), so they produce the same bits.  Merging with an empty
+// record gives the other operand exactly, so records past G are empty ones and skipped work
+// changes no bits.
+static_assert(kMaxVocabGroups == kGroup * kGroup, "two levels of 16 cover every range");
 
 // ----------------------------------------------------------------------------------------------
 // Element-type traits: one 16-byte fragment per lane feeds one bf16 MFMA (16x16x32) or four
@@ -637,7 +652,7 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 //     rs_g = 1 for the records of one head's workgroups; rs_row = 1, rs_g = B*L for gathered
 //     vocabulary shards), G <= kMaxVocabGroups.  One 16-lane row per row of the block: lane j
 //     loads group j's records and merges them in registers, then the 16 lanes merge the groups
-//     (merge_records' tree, four rows per wavefront at once).
+//     (the two-level tree, four rows per wavefront at once).
 //   GROUPED = true: `rec` holds the second-level records of the distributed merge, G <= kGroup per
 //     row at r*rs_row + g; one 16-lane row per row of the block (the second level of the same tree).
 // IN_KERNEL: `rec` may have been written by other workgroups of the running kernel (or outside
@@ -666,9 +681,10 @@ __device__ __forceinline__ void finalize_row(const CommitArgs& c, const Stats& t
   s_gap[rr] = t.m1 - t.m2;
 }
 
-template <bool GROUPED, bool IN_KERNEL>
+template <bool GROUPED, bool IN_KERNEL, bool TK = false>
 __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t rec, int G, int rs_row, int rs_g,
-                                   int b_begin, int b_end, uint4* smem, const SeqState& pre, int pre_b) {
+                                   int b_begin, int b_end, uint4* smem, const SeqState& pre, int pre_b,
+                                   __amdgpu_buffer_rsrc_t trec) {
   const int tid = lid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool do_commit = (c.flags & kFlagCommit) != 0;
@@ -682,16 +698,23 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
     // 4 rows per wavefront pass, one per 16-lane row; lane j of a row takes group j
     if constexpr (GROUPED) {
       // one record per lane: two passes per iteration, both loads before the first merge, so
-      // up to 64 rows cost one round trip
+      // up to 64 rows cost one round trip.  With TK the lane also loads its group's merged
+      // top-k list (64 bytes at [row][group] in trec) and the row's 16 lanes merge the lists.
       for (int rr0 = wave * 4; rr0 < nrows; rr0 += 2 * kWaves * 4) {
         const int j = lane & 15;
         float4 v[2];
+        float4 e[TK ? 2 : 1][kTopK / 2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int rr = rr0 + h * kWaves * 4 + (lane >> 4);
           const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
           const unsigned o = j < G && rr < nrows ? src + 16u * (unsigned)(j * rs_g) : 0x80000000u;
           v[h] = IN_KERNEL ? record_load(rec, o) : record_load_after_kernel(rec, o);
+          if constexpr (TK) {
+#pragma unroll
+            for (int q = 0; q < kTopK / 2; ++q)
+              e[h][q] = record_load(trec, o == 0x80000000u ? o : o * (unsigned)(kTopK / 2) + 16u * q);
+          }
         }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -699,6 +722,16 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
           if (rr0 + h * kWaves * 4 >= nrows) break;   // (uniform: no row of this pass exists)
           const Stats t = stats_row16_merge(stats_unpack(j < G ? v[h] : stats_pack(stats_empty())));
           if (rr < nrows && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
+          if constexpr (TK) {
+            TopK mine, best;
+            if (j < G) {
+              topk_from_records(mine, e[h]);
+            } else {
+              topk_clear(mine);
+            }
+            topk_row16_merge(mine, best);
+            if (rr < nrows) topk_write_row(c, best, r_first + rr, j, t.m1, 1.f / t.s);
+          }
         }
       }
     } else
@@ -772,8 +805,9 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
 // commit policy on one wavefront.
 //
 // With TK (top-k export) every thread also keeps the DLM_MAX_TOPK best logits of its slot, the
-// workgroup merges them per row into a second record, and the kernel ends there:
-// finalize_topk_kernel merges, commits and writes the export.
+// workgroup merges them per row into a second record (a best-first list), and the two merge
+// levels merge the lists next to the statistics: 16 ranges' lists per row by the group's last
+// workgroup, then the groups' lists by the last group, which writes the export.
 // ----------------------------------------------------------------------------------------------
 template <class T, int NMB, int KFWM, bool TK>
 __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
@@ -982,10 +1016,7 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
             a.topk_records, 0, a.n_rg * MR * a.G_v * (kTopK * 8), 0x00020000);
         const unsigned off = (unsigned)((((size_t)rg * MR + rr) * a.G_v + gv) * (kTopK * 8));
 #pragma unroll
-        for (int j = 0; j < kTopK / 2; ++j)
-          record_store(trec, off + 16u * j,
-                       make_float4(best.z[2 * j], __int_as_float(best.id[2 * j]), best.z[2 * j + 1],
-                                   __int_as_float(best.id[2 * j + 1])));
+        for (int j = 0; j < kTopK / 2; ++j) record_store(trec, off + 16u * j, topk_record(best, j));
       }
     }
   }
@@ -993,12 +1024,11 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   // cache write-back, only the wait for their acknowledgement.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if constexpr (TK) return;   // finalize_topk_kernel follows on the stream
 
   // ---- two-level merge across workgroups --------------------------------------------------------
   // The records of each group of kGroup consecutive vocabulary ranges are merged, row by row, by
   // the group's last workgroup to finish; the last group to finish then merges the groups'
-  // records of every row and commits (the two levels of merge_records' tree).  Each counter is
+  // records of every row and commits (the two levels of the merge tree).  Each counter is
   // incremented with wrap-around: it runs 0 .. n-1 and its last arrival puts it back to 0, so a
   // workspace that starts zeroed is zero again between calls.
   __shared__ int s_last;
@@ -1016,12 +1046,24 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   // passes (two at 64 rows) share one round trip to the coherence point
   constexpr int kPasses = (MR + kWaves * 4 - 1) / (kWaves * 4);
   float4 gv_rec[kPasses];
+  float4 gv_list[TK ? kPasses : 1][kTopK / 2];            // with TK: the ranges' top-k lists
+  const __amdgpu_buffer_rsrc_t trec = __builtin_amdgcn_make_buffer_rsrc(
+      TK ? a.topk_records : a.partials, 0, TK ? a.n_rg * MR * a.G_v * (kTopK * 8) : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t tl2 = __builtin_amdgcn_make_buffer_rsrc(
+      TK ? a.topk_level2 : a.level2, 0, TK ? a.n_rg * MR * a.nq * (kTopK * 8) : 0, 0x00020000);
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
     const int rr = pass * kWaves * 4 + wave * 4 + (lane >> 4);
     const int j = lane & 15, g = kGroup * grp + j;
     const unsigned row = (unsigned)(rg * MR + rr);
-    gv_rec[pass] = record_load(rec, g < a.G_v && rr < MR ? (row * (unsigned)a.G_v + (unsigned)g) * 16u : 0x80000000u);
+    const bool in = g < a.G_v && rr < MR;
+    gv_rec[pass] = record_load(rec, in ? (row * (unsigned)a.G_v + (unsigned)g) * 16u : 0x80000000u);
+    if constexpr (TK) {
+#pragma unroll
+      for (int q = 0; q < kTopK / 2; ++q)
+        gv_list[pass][q] =
+            record_load(trec, in ? (row * (unsigned)a.G_v + (unsigned)g) * (kTopK * 8u) + 16u * q : 0x80000000u);
+    }
   }
 #pragma unroll
   for (int pass = 0; pass < kPasses; ++pass) {
@@ -1032,6 +1074,20 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
     const float4 v = g < a.G_v ? gv_rec[pass] : stats_pack(stats_empty());
     const Stats t = stats_row16_merge(stats_unpack(v));
     if (j == 0) record_store(l2, (row * (unsigned)a.nq + (unsigned)grp) * 16u, stats_pack(t));
+    if constexpr (TK) {
+      TopK mine, best;
+      if (g < a.G_v) {
+        topk_from_records(mine, gv_list[pass]);
+      } else {
+        topk_clear(mine);
+      }
+      topk_row16_merge(mine, best);
+      if (j == 0) {
+#pragma unroll
+        for (int q = 0; q < kTopK / 2; ++q)
+          record_store(tl2, (row * (unsigned)a.nq + (unsigned)grp) * (kTopK * 8u) + 16u * q, topk_record(best, q));
+      }
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);              // the group's records are out before it is counted
   __syncthreads();
@@ -1049,7 +1105,13 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   if (!s_last) return;
 
-  finalize_sequences<true, true>(c, l2, a.nq, a.nq, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1);
+  if constexpr (TK) {
+    const __amdgpu_buffer_rsrc_t tl2 =
+        __builtin_amdgcn_make_buffer_rsrc(a.topk_level2, 0, a.n_rg * MR * a.nq * (kTopK * 8), 0x00020000);
+    finalize_sequences<true, true, true>(c, l2, a.nq, a.nq, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1, tl2);
+  } else {
+    finalize_sequences<true, true>(c, l2, a.nq, a.nq, 1, 0, c.B, smem, pre, wave < c.B ? wave : -1, l2);
+  }
 }
 
 // ----------------------------------------------------------------------------------------------
@@ -1506,102 +1568,6 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
   }
 }
 
-// Top-k export of one row (one wavefront).  Lane l holds the row's best-first lists g = l, l + 64,
-// ... (empty past G).  Each round the wave takes the best head (largest logit, then lowest id);
-// only the lane that held it pops that list and re-scans its heads, inside a branch, so a round
-// costs two wave reductions and one lane's update.  A candidate's probability is
-// 2^((z - M) log2 e) / S with the row's maximum M and sum S, so entry 0 equals the confidence.
-template <int N>
-__device__ __forceinline__ void topk_merge_row(const CommitArgs& c, TopK (&t)[N], int row, float M, float inv_s) {
-  const int lane = __lane_id();
-  auto best_head = [&](float& bz, int& bi, int& bn) {
-    bz = t[0].z[0];
-    bi = t[0].id[0];
-    bn = 0;
-#pragma unroll
-    for (int n = 1; n < N; ++n) {
-      const bool better = t[n].z[0] > bz || (t[n].z[0] == bz && t[n].id[0] < bi);
-      bz = better ? t[n].z[0] : bz;
-      bi = better ? t[n].id[0] : bi;
-      bn = better ? n : bn;
-    }
-  };
-  float bz;
-  int bi, bn;
-  best_head(bz, bi, bn);
-  const size_t out0 = (size_t)row * c.topk;
-  for (int r = 0; r < c.topk; ++r) {
-    const float m = wave_max(bz);
-    const int id = wave_allreduce_min(bz == m ? bi : kNoToken);
-    if (bz == m && bi == id && id != kNoToken) {   // the one lane holding the winner
-#pragma unroll
-      for (int n = 0; n < N; ++n)
-        if (bn == n) topk_pop_if(t[n], true);
-      best_head(bz, bi, bn);
-    }
-    if (lane == 0) {
-      const bool real = id != kNoToken;
-      c.out_topk_tokens[out0 + r] = real ? id : -1;
-      if (c.out_topk_prob) c.out_topk_prob[out0 + r] = real ? fminf(ex2((m - M) * kLog2e) * inv_s, 1.f) : 0.f;
-    }
-  }
-}
-
-// Merge + commit after the streaming kernel with the top-k fold.  Workgroups [0, B) merge and
-// commit one sequence each (finalize_sequences); the others take one row per wavefront: they merge
-// its statistics records again (same order, same result) for M and S, then its top-k records.
-// Every load of a row is issued before the first wait (records past G read as out of range and
-// are replaced by empty values), so a row costs one round trip to memory.
-__global__ __launch_bounds__(kThreads) void finalize_topk_kernel(const CommitArgs c, const float4* records,
-                                                                 const float4* topk_records, int G,
-                                                                 int nrows_total) {
-  constexpr int N = kMaxVocabGroups / 64;
-  __shared__ uint4 stage[kRowsPerStage * 12 / 16];
-  const int wave = __builtin_amdgcn_readfirstlane(lid() >> 6);
-  const __amdgpu_buffer_rsrc_t rec =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
-  if (gid() < c.B) {
-    const int b = gid();
-    SeqState pre;
-    const bool do_commit = (c.flags & kFlagCommit) != 0;
-    if (do_commit && wave == 0) pre = load_seq_state(c, b);
-    finalize_sequences<false, false>(c, rec, G, G, 1, b, b + 1, stage, pre, wave == 0 ? b : -1);
-    return;
-  }
-  const int row = (gid() - c.B) * kWaves + wave;
-  if (row >= c.B * c.L) return;
-  const int lane = lid() & 63;
-  const __amdgpu_buffer_rsrc_t trec = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float4*>(topk_records), 0, nrows_total * G * (kTopK * 8), 0x00020000);
-  constexpr unsigned kOOB = 0x80000000u;   // beyond any range: the load returns zeros
-  float4 r[N];
-  float4 e[N][kTopK / 2];
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const int gs = record_of_lane(lane, n);   // statistics: merge_records' layout
-    r[n] = record_load_after_kernel(rec, gs < G ? (unsigned)(((size_t)row * G + gs) * 16) : kOOB);
-    const int g = lane + 64 * n;              // lists: any layout (they merge by value)
-#pragma unroll
-    for (int j = 0; j < kTopK / 2; ++j)
-      e[n][j] = record_load_after_kernel(trec, g < G ? (unsigned)(((size_t)row * G + g) * (kTopK * 8) + 16 * j) : kOOB);
-  }
-  TopK t[N];
-#pragma unroll
-  for (int n = 0; n < N; ++n) {
-    const bool in = lane + 64 * n < G;
-    r[n] = record_of_lane(lane, n) < G ? r[n] : stats_pack(stats_empty());
-#pragma unroll
-    for (int j = 0; j < kTopK / 2; ++j) {
-      t[n].z[2 * j] = in ? e[n][j].x : -INFINITY;
-      t[n].id[2 * j] = in ? __float_as_int(e[n][j].y) : kNoToken;
-      t[n].z[2 * j + 1] = in ? e[n][j].z : -INFINITY;
-      t[n].id[2 * j + 1] = in ? __float_as_int(e[n][j].w) : kNoToken;
-    }
-  }
-  const Stats st = merge_records(r, G);
-  topk_merge_row<N>(c, t, row, st.m1, 1.f / st.s);
-}
-
 // Merge + commit of gathered vocabulary shards (records [G][B*L], shards in vocabulary order):
 // the same merge and commit as the single-GPU head's, one workgroup per sequence.
 __global__ __launch_bounds__(kThreads) void merge_commit_kernel(const CommitArgs c, const float4* records, int G) {
@@ -1615,7 +1581,7 @@ __global__ __launch_bounds__(kThreads) void merge_commit_kernel(const CommitArgs
   if (wave == 0) pre = load_seq_state(c, b);
   // (the gathered records may have been written by a copy or by another device: device-scope
   // loads, as in the in-kernel merge)
-  finalize_sequences<false, true>(c, rec, G, 1, M, b, b + 1, stage, pre, wave == 0 ? b : -1);
+  finalize_sequences<false, true>(c, rec, G, 1, M, b, b + 1, stage, pre, wave == 0 ? b : -1, rec);
 }
 
 // dlm_commit: conf / tokens given, one wavefront per sequence.

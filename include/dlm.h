@@ -151,8 +151,8 @@ typedef struct {
  *                          exp(z - max z) / sum_v exp(z_v - max z), so entry 0 is the confidence;
  *   entries past V         token -1, probability 0.
  * The workspace must hold dlm_workspace_bytes_topk(B, L, H, V, dtype, topk) bytes.  With top-k
- * on, every shape takes the streaming LM head (the GEMM-shaped head for B*L > 64 has no top-k
- * fold), followed by a separate merge kernel.  Errors: topk outside 0..DLM_MAX_TOPK gives
+ * on, every shape takes the streaming LM head (one kernel: the lists are merged with the
+ * statistics).  Errors: topk outside 0..DLM_MAX_TOPK gives
  * DLM_ERR_POLICY, topk > 0 with out_topk_tokens NULL gives DLM_ERR_NULL, a workspace smaller
  * than the top-k size gives DLM_ERR_WORKSPACE.
  */

@@ -206,14 +206,15 @@ def test_decode_steps_validation():
 
 def test_topk_workspace_sizes():
     # top-k on: the streaming plan for every shape, plus one list of 8 (logit, id) pairs (64 bytes)
-    # per (padded row, vocabulary range) after the statistics records
+    # per (padded row, vocabulary range) after the statistics records, then one merged list per
+    # (padded row, group of 16 ranges)
     base = 256 + 32 * 256 * 16 + 32 * 16 * 16
-    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 8) == base + 32 * 256 * 64
-    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 3) == base + 32 * 256 * 64
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 8) == base + 32 * 256 * 64 + 32 * 16 * 64
+    assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 3) == base + 32 * 256 * 64 + 32 * 16 * 64
     # 512 bf16 rows: 64-row groups (8 of them), 32 vocabulary ranges (2 groups) each, no packed
     # hidden rows
     assert nat.dlm_workspace_bytes_topk(16, 32, 2048, 157184, nat.DLM_BF16, 8) == \
-        256 + 512 * 32 * 16 + 512 * 2 * 16 + 512 * 32 * 64
+        256 + 512 * 32 * 16 + 512 * 2 * 16 + 512 * 32 * 64 + 512 * 2 * 64
     for B, L, H, V, dt in [(1, 32, 2048, 126464, 1), (16, 32, 2048, 157184, 1), (1, 8, 64, 1024, 0)]:
         assert nat.dlm_workspace_bytes_topk(B, L, H, V, dt, 0) == nat.dlm_workspace_bytes(B, L, H, V, dt)
     assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 9) == 0
