@@ -368,7 +368,7 @@ def main():
         }
         print(json.dumps(out), flush=True)
         return
-    gemm_path = not args.topk and wl.dtype == "bf16" and wl.B * wl.L > 64 and wl.H % 256 == 0
+    gemm_path = wl.dtype == "bf16" and wl.B * wl.L > 64 and wl.H % 256 == 0
     one_kernel = not gemm_path                            # the step is the head kernel itself
     head = None
     if args.loop == "calls":
@@ -393,7 +393,8 @@ def main():
     if args.topk and one_kernel:
         roof["kernel"] = "dlm::step_kernel with the top-k fold (one launch per step)"
     elif gemm_path:
-        gemm = "dlm::gemm_r512_kernel" if wl.B * wl.L > 256 else "dlm::gemm_r256_kernel"
+        gemm = ("dlm::gemm_r512_topk_kernel" if args.topk else
+                "dlm::gemm_r512_kernel" if wl.B * wl.L > 256 else "dlm::gemm_r256_kernel")
         roof["kernel"] = gemm + " (the step also holds pack_hidden_kernel and finalize_parts_kernel)"
     else:
         roof["kernel"] = "dlm::step_kernel (one launch per step)"

@@ -51,7 +51,7 @@ struct Plan {
   size_t ws = 0;     // workspace bytes
   size_t packed_off = 0, packed_bytes = 0;  // GEMM path: fragment-ordered hidden rows in the workspace
   size_t rowout_off = 0;                    // GEMM path: published per-row conf / token / gap [B*L]
-  int topk = 0;      // streaming kernel with the top-k fold (merged with the statistics in-kernel)
+  int topk = 0;      // kernels with the top-k fold
   size_t topk_off = 0;                      // top-k records in the workspace
   size_t topk_l2_off = 0;                   // second-level top-k records [rows][nq] x 64 bytes
   int nq = 0;        // streaming kernel: groups of dlm::kGroup vocabulary ranges (two-level merge)
@@ -61,8 +61,9 @@ struct Plan {
 
 int elem_bytes(int32_t dtype) { return dtype == DLM_BF16 ? 2 : dtype == DLM_F32 ? 4 : 0; }
 
-// topk > 0 selects the streaming kernel with the top-k fold for every shape (the GEMM-shaped head
-// has none) and appends its records to the workspace; the caller validates topk's range.
+// topk > 0 selects the kernels with the top-k fold (the 512-row GEMM-shaped head beyond 64 bf16
+// rows, else the streaming kernel) and appends their lists to the workspace; the caller validates
+// topk's range.
 // fixed_ticket_bytes > 0 places the counters in a region of that size at the start of the
 // workspace whatever the shapes (the records follow it), so that calls of different shapes
 // sharing one workspace never find another shape's records where their counters are.
@@ -78,11 +79,13 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
   const int64_t ntiles = (V + dlm::kTileRows - 1) / dlm::kTileRows;
   if (ntiles > (1ll << 26)) return fail(DLM_ERR_SHAPE, "V=%lld too large", (long long)V);
   const int64_t m_pad = (M + 31) / 32 * 32;
-  if (!topk && dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && m_pad * H * 2 < (1ll << 31)) {
+  if (dtype == DLM_BF16 && M > 64 && H % 256 == 0 && V * H * 2 < (1ll << 31) - 64 && m_pad * H * 2 < (1ll << 31) &&
+      (!topk || V < dlm::kMaxGemmTopkV)) {
     // GEMM-shaped path: 256-row vocabulary tiles against 256-row groups up to 256 rows, 128-row
     // tiles against 512-row groups beyond; workgroups per row group a multiple of 8 where
-    // possible (so the groups of one tile can share an XCD)
-    const bool r512 = M > dlm::GemmR256::Rows;
+    // possible (so the groups of one tile can share an XCD).  The top-k fold exists for the
+    // 512-row shape only (its chunk lists need LDS the 256-row shape's ring leaves no room for).
+    const bool r512 = M > dlm::GemmR256::Rows || topk;
     const int64_t BN = r512 ? dlm::GemmR512::BN : dlm::GemmR256::BN;
     const int64_t rows = r512 ? dlm::GemmR512::Rows : dlm::GemmR256::Rows;
     const int64_t nt = (V + BN - 1) / BN;
@@ -109,6 +112,13 @@ int make_plan(int64_t B, int64_t L, int64_t H, int64_t V, int32_t dtype, int top
     p->packed_bytes = (size_t)m_pad * H * 2;
     p->rowout_off = p->packed_off + p->packed_bytes;
     p->ws = p->rowout_off + (size_t)M * 16;
+    if (topk) {
+      // ... | chunk lists [G_t][n_rg * rows] x DLM_MAX_TOPK x 8 bytes
+      if (n_rg * rows * G_t * (DLM_MAX_TOPK * 8) >= (1ll << 31)) return fail(DLM_ERR_SHAPE, "B*L too large for top-k");
+      p->topk = 1;
+      p->topk_off = p->ws;
+      p->ws += (size_t)n_rg * rows * G_t * (DLM_MAX_TOPK * 8);
+    }
     return DLM_OK;
   }
   // each wavefront holds ceil(F / 8) hidden fragments per 16-row block in registers
@@ -300,22 +310,39 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     g.n_rg = p.n_rg;
     g.G_t = p.G_v;
     g.ntiles = p.ntiles;
+    g.topk_records = p.topk ? reinterpret_cast<uint4*>(static_cast<char*>(pol->workspace) + p.topk_off) : nullptr;
+    g.id_bits = 1;
+    while ((1ll << g.id_bits) <= (long long)a.V) ++g.id_bits;   // bit length of V: all ones is no token
     const bool r512 = p.gemm == dlm::GemmR512::Rows;
     const dim3 grid(p.n_rg * p.G_v), block(r512 ? dlm::GemmR512::Threads : dlm::GemmR256::Threads);
     const int rows = p.gemm;
     const bool tail = a.V % (r512 ? dlm::GemmR512::BN : dlm::GemmR256::BN) != 0;
     if ((rc = head_event(pol, time_head, 0, stream))) return rc;
-    if (r512)
+    if (p.topk)
+      hipLaunchKernelGGL(tail ? dlm::gemm_r512_topk_tail_kernel : dlm::gemm_r512_topk_kernel, grid, block, 0, stream, g);
+    else if (r512)
       hipLaunchKernelGGL(tail ? dlm::gemm_r512_tail_kernel : dlm::gemm_r512_kernel, grid, block, 0, stream, g);
     else
       hipLaunchKernelGGL(tail ? dlm::gemm_r256_tail_kernel : dlm::gemm_r256_kernel, grid, block, 0, stream, g);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "gemm kernel launch: %s", hipGetErrorString(e));
     if ((rc = head_event(pol, time_head, 1, stream))) return rc;
-    const int parts = (c.L + dlm::kFinRows - 1) / dlm::kFinRows;
-    hipLaunchKernelGGL(dlm::finalize_parts_kernel, dim3(c.B * parts), dim3(128), 0, stream, a.c, a.partials,
-                       p.G_v, p.n_rg * rows, a.ticket,
-                       reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.rowout_off));
+    const int fin_rows = p.topk ? dlm::kFinRowsTopk : dlm::kFinRows;
+    const int parts = (c.L + fin_rows - 1) / fin_rows;
+    dlm::GemmTopkArgs tka;
+    tka.lists = g.topk_records;
+    tka.W = W;
+    tka.hidden = hidden;
+    tka.H = a.H;
+    tka.V = a.V;
+    tka.id_bits = g.id_bits;
+    float4* const row_out = reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.rowout_off);
+    if (p.topk)
+      hipLaunchKernelGGL(dlm::finalize_parts_kernel<true>, dim3(c.B * parts), dim3(64 * dlm::kFinRowsTopk), 0, stream,
+                         a.c, a.partials, p.G_v, p.n_rg * rows, a.ticket, row_out, tka);
+    else
+      hipLaunchKernelGGL(dlm::finalize_parts_kernel<false>, dim3(c.B * parts), dim3(128), 0, stream, a.c, a.partials,
+                         p.G_v, p.n_rg * rows, a.ticket, row_out, tka);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "finalize kernel launch: %s", hipGetErrorString(e));
     return ok();

@@ -1192,7 +1192,52 @@ struct GemmArgs {
   int ntiles;                 // ceil(V / tile rows)
   unsigned packed_bytes;      // bytes of hidden_packed
   unsigned fold_gate;         // all ones (see fold_tile)
+  uint4* topk_records;        // top-k fold only: [G_t][n_rg * rows per group] chunk lists, 64 bytes each
+  int id_bits;                // top-k fold only: bit length of V (chunk entries)
 };
+
+// ---- top-k on the GEMM-shaped head: lists of chunk maxima ---------------------------------------
+// A lane's 16 logits of one 32-row vocabulary block of a tile (ids 32vb + 8q + 4h + r, q, r < 4,
+// h = lane / 32) form a chunk.  The fold already finds each chunk's maximum, its lowest arg-max
+// and its second-largest value; with the top-k export each lane also keeps, per hidden row, the
+// best kTopK chunks by (maximum desc, arg-max id asc), in LDS.  The row's k best tokens lie in the
+// k best chunks (each of those has its maximum at or above the k-th best chunk maximum T, and any
+// token outside them is at or below T and loses to all k maxima, ties by id), and inside such a
+// chunk a token other than its maximum can only qualify when the chunk's second value reaches T;
+// those few chunks are recomputed exactly in the finalizer.
+// An entry is (maximum, id | gap code << id_bits), id_bits = bit length of V (so the all-ones id
+// is no token).  The code is a lower bound on the gap g = maximum - second in a small float format
+// (4 exponent bits for g in [2^-7, 2^8), the remaining 28 - id_bits bits of mantissa, truncated
+// and then lowered by one unit; 0 = below 2^-7, all ones = 2^8 or more), so maximum - bound(code)
+// bounds the second value from above.
+constexpr int kMaxGemmTopkV = 1 << 22;                    // id_bits <= 22: at least 6 mantissa bits
+
+__device__ __forceinline__ unsigned chunk_gap_code(float m, float m2, int id_bits) {
+  const int mb = 28 - id_bits;                            // mantissa bits of the code
+  const float g = m - m2;                                 // +inf when the chunk has one valid logit
+  if (!(g >= 0.0078125f)) return 0u;                      // below 2^-7 (or no second value: never here)
+  const unsigned bits = __float_as_uint(g);
+  const int e = (int)(bits >> 23) - 127;
+  if (e >= 8) return (1u << (32 - id_bits)) - 1u;         // 2^8 or more (and +inf)
+  const unsigned c = ((unsigned)(e + 8) << mb) | ((bits & 0x7FFFFFu) >> (23 - mb));
+  return c > (1u << mb) ? c - 1u : 0u;
+}
+
+__device__ __forceinline__ float chunk_gap_bound(unsigned code, int id_bits) {
+  const int mb = 28 - id_bits;
+  const unsigned e = code >> mb;
+  if (e == 0) return 0.f;
+  return __uint_as_float(((e + 119u) << 23) | ((code & ((1u << mb) - 1u)) << (23 - mb)));
+}
+
+// (z, id) of entry a before entry b: larger maximum first, lower id on ties (bitwise, so that the
+// compiler emits selects rather than a branch per operand)
+__device__ __forceinline__ bool chunk_before(uint2 a, uint2 b, unsigned id_mask) {
+  const float za = __uint_as_float(a.x), zb = __uint_as_float(b.x);
+  return (za > zb) | ((za == zb) & ((a.y & id_mask) < (b.y & id_mask)));
+}
+
+__device__ __forceinline__ uint2 chunk_empty(unsigned id_mask) { return make_uint2(__float_as_uint(-INFINITY), id_mask); }
 
 // Hidden rows -> MFMA fragment order: fragment (rb, kg) is 1 KB at (rb * H/16 + kg) * 1 KB, lane l
 // holding row 32rb + l%32, elements 16kg + 8(l/32) .. +8.  Rows past M are zero.
@@ -1231,9 +1276,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 // >= lim from v0 (ids >= V, last tile) become -inf first.
 // Each 16-logit chunk sits behind its own bit of `gate` (all ones at run time): separate basic
 // blocks keep the compiler from interleaving chunks, which would hold every logit in registers.
-template <class G, int HB, bool TAIL>
+template <class G, int HB, bool TAIL, bool TK>
 __device__ __forceinline__ void fold_tile(Stats& st, const f32x16 (&acc)[G::VB][G::HB], int v0, int lim,
-                                          unsigned gate) {
+                                          unsigned gate, uint2* list, int id_bits) {
 #pragma unroll
   for (int vb = 0; vb < G::VB; ++vb) {
     if (!((gate >> (G::VB * HB + vb)) & 1u)) continue;
@@ -1282,29 +1327,51 @@ __device__ __forceinline__ void fold_tile(Stats& st, const f32x16 (&acc)[G::VB][
     st.m2 = fmaxf(fmaxf(st.m2, m2), fminf(st.m1, m));
     st.id = m > st.m1 ? v0 + 32 * vb + id : st.id;        // ids of this chunk exceed earlier ones
     st.m1 = mnew;
+    if constexpr (TK) {
+      // the chunk enters this lane's list (entries [i * 64], best first) where it beats the last
+      // entry: it is carried down the list, swapping with every entry it beats (chunks arrive in
+      // ascending id order, so it goes behind equal maxima)
+      const bool enter = m > __uint_as_float(list[(kTopK - 1) * 64].x);
+      if (__builtin_amdgcn_ballot_w64(enter)) {
+        if (enter) {
+          const unsigned id_mask = (1u << id_bits) - 1u;
+          uint2 carry = make_uint2(__float_as_uint(m),
+                                   (unsigned)(v0 + 32 * vb + id) | (chunk_gap_code(m, m2, id_bits) << id_bits));
+#pragma unroll
+          for (int i = 0; i < kTopK; ++i) {
+            const uint2 e = list[i * 64];
+            const bool b = chunk_before(carry, e, id_mask);
+            list[i * 64] = make_uint2(b ? carry.x : e.x, b ? carry.y : e.y);
+            carry = make_uint2(b ? e.x : carry.x, b ? e.y : carry.y);
+          }
+        }
+      }
+    }
   }
 }
 
 // The running statistics live in LDS between folds (st[hb * 64 + lane]): they are touched once
 // per tile, and registers are what the streaming loop needs.
-template <class G, int HB, bool TAIL>
+template <class G, int HB, bool TAIL, bool TK>
 __device__ __forceinline__ void fold_all(float4* st, const f32x16 (&acc)[G::VB][G::HB], int v0, int lim,
-                                         unsigned gate) {
+                                         unsigned gate, uint2* lists, int id_bits) {
   Stats t = stats_unpack(st[HB * 64]);
-  fold_tile<G, HB, TAIL>(t, acc, v0, lim, gate);
+  fold_tile<G, HB, TAIL, TK>(t, acc, v0, lim, gate, lists + HB * kTopK * 64, id_bits);
   st[HB * 64] = stats_pack(t);
-  if constexpr (HB + 1 < G::HB) fold_all<G, HB + 1, TAIL>(st, acc, v0, lim, gate);
+  if constexpr (HB + 1 < G::HB) fold_all<G, HB + 1, TAIL, TK>(st, acc, v0, lim, gate, lists, id_bits);
 }
 
 // TAIL: V is not a multiple of the tile, so the last tile's padding ids are masked in the fold (a
 // separate instantiation keeps that code out of the common case).
-template <class G, bool TAIL>
+template <class G, bool TAIL, bool TK = false>
 __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
   // W stage buffers [row * 8 + permuted chunk], one array each so that the compiler can tell a
   // buffer being filled from the one being read (it would otherwise wait for every fill)
   __shared__ uint4 wring0[G::Slot], wring1[G::Slot], wring2[G::Slot], wring3[G::Slot];
   auto ring = [&](int slot) -> uint4* { return slot == 0 ? wring0 : slot == 1 ? wring1 : slot == 2 ? wring2 : wring3; };
   __shared__ float4 st_lds[G::Waves * G::HB * 64];    // running statistics, [wave][hb][lane]
+  // top-k: [wave][hb][entry][lane] chunk lists (kTopK entries of 8 bytes per lane and hidden row)
+  __shared__ uint2 tk_lds[TK ? G::Waves * G::HB * kTopK * 64 : 1];
   const int tid = lid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // workgroups of one vocabulary range (one per row group) sit 8 block indices apart: one XCD
@@ -1382,6 +1449,13 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
   float4* const st = st_lds + wave * (G::HB * 64) + lane;
 #pragma unroll
   for (int hb = 0; hb < G::HB; ++hb) st[hb * 64] = stats_pack(stats_empty());
+  uint2* const lists = tk_lds + (TK ? wave * (G::HB * kTopK * 64) + lane : 0);
+  const int id_bits = TK ? __builtin_amdgcn_readfirstlane(a.id_bits) : 0;
+  const unsigned id_mask = (1u << id_bits) - 1u;
+  if constexpr (TK) {
+#pragma unroll
+    for (int i = 0; i < G::HB * kTopK; ++i) lists[i * 64] = chunk_empty(id_mask);
+  }
 
   // prologue: W stages 0..2, hidden stages 0 .. depth-1, then the barrier that opens stage 0.
   // Every W load of the prologue has at least G::VmAfterW vector-memory instructions behind it
@@ -1460,7 +1534,7 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
     // tile done: fold its logits (the next tile's loads are in flight)
     const int t0 = (gi + ti * a.G_t) * G::BN;
     const int v0 = t0 + 4 * (lane >> 5);
-    fold_all<G, 0, TAIL>(st, acc, v0, a.V - v0, a.fold_gate);  // ids >= V are skipped
+    fold_all<G, 0, TAIL, TK>(st, acc, v0, a.V - v0, a.fold_gate, lists, id_bits);  // ids >= V are skipped
   }
   __builtin_amdgcn_s_waitcnt(0);                          // no load into LDS may outlive the workgroup
 
@@ -1479,6 +1553,43 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
     const Stats t = stats_merge(lo, hi);
     const unsigned row = h_row0 + 32u * hb;
     if (lane < 32 && (int)row < a.M) a.records[(size_t)gi * (a.n_rg * G::Rows) + row] = stats_pack(t);
+    if constexpr (TK) {
+      // the two lanes' chunk lists of the row -> its k best chunks (a bitonic merge: the better
+      // of A[i] and B[k-1-i] for every i, then three compare-exchange stages)
+      uint2 A[kTopK], B[kTopK], C[kTopK];
+#pragma unroll
+      for (int i = 0; i < kTopK; ++i) {
+        const uint2 e = lists[(hb * kTopK + i) * 64];
+        int x0, x1, y0, y1;
+        row_swap<32>((int)e.x, x0, x1);
+        row_swap<32>((int)e.y, y0, y1);
+        A[i] = make_uint2((unsigned)x0, (unsigned)y0);
+        B[i] = make_uint2((unsigned)x1, (unsigned)y1);
+      }
+#pragma unroll
+      for (int i = 0; i < kTopK; ++i) {
+        const bool a = chunk_before(A[i], B[kTopK - 1 - i], id_mask);  // (selects per component: no indexing)
+        C[i].x = a ? A[i].x : B[kTopK - 1 - i].x;
+        C[i].y = a ? A[i].y : B[kTopK - 1 - i].y;
+      }
+#pragma unroll
+      for (int d = kTopK / 2; d >= 1; d /= 2)
+#pragma unroll
+        for (int i = 0; i < kTopK; ++i)
+          if ((i & d) == 0) {
+            const bool keep = chunk_before(C[i], C[i + d], id_mask);
+            const unsigned x0 = C[i].x, x1 = C[i].y, y0 = C[i + d].x, y1 = C[i + d].y;
+            C[i].x = keep ? x0 : y0;
+            C[i].y = keep ? x1 : y1;
+            C[i + d].x = keep ? y0 : x0;
+            C[i + d].y = keep ? y1 : x1;
+          }
+      if (lane < 32 && (int)row < a.M) {
+        uint4* dst = a.topk_records + ((size_t)gi * (a.n_rg * G::Rows) + row) * (kTopK / 2);
+#pragma unroll
+        for (int q = 0; q < kTopK / 2; ++q) dst[q] = make_uint4(C[2 * q].x, C[2 * q].y, C[2 * q + 1].x, C[2 * q + 1].y);
+      }
+    }
   }
 }
 
@@ -1487,6 +1598,12 @@ __global__ __launch_bounds__(GemmR256::Threads) void gemm_r256_kernel(const Gemm
 __global__ __launch_bounds__(GemmR256::Threads) void gemm_r256_tail_kernel(const GemmArgs a) { gemm_stats<GemmR256, true>(a); }
 __global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_kernel(const GemmArgs a) { gemm_stats<GemmR512, false>(a); }
 __global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_tail_kernel(const GemmArgs a) { gemm_stats<GemmR512, true>(a); }
+__global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_topk_kernel(const GemmArgs a) {
+  gemm_stats<GemmR512, false, true>(a);
+}
+__global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_topk_tail_kernel(const GemmArgs a) {
+  gemm_stats<GemmR512, true, true>(a);
+}
 
 // Merge + commit after the GEMM-path kernel, spread over more compute units: workgroup
 // (b, part) merges rows kFinRows*part .. +kFinRows-1 of sequence b (two wavefronts of four rows,
@@ -1498,22 +1615,223 @@ __global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_tail_kernel(const
 //     after every call) commits the sequence from the published values.
 // records: [G][nrows_total] (the GEMM kernels' layout).  Grid: B x ceil(L / kFinRows) workgroups of
 // 128 threads.  tickets: [B] counters; row_out: [B*L] 16-byte values.
+// With TK (top-k export after gemm_r512_topk_kernel) a workgroup takes kFinRowsTopk rows, one per
+// wavefront (its four 16-lane rows merge the same row's statistics, with the same tree), and each
+// wavefront also writes its row's export (gemm_topk_row).
 constexpr int kFinRows = 8;
+constexpr int kFinRowsTopk = 2;   // with the top-k export: one row per wavefront, two per workgroup
+
+// Exact logits of one chunk (vocabulary rows base32 + 8q + 4h + r, q, r < 4) against hidden row
+// `row`, by the same v_mfma_f32_32x32x16_bf16 sequence as the GEMM kernels (the same operands for
+// the row's column, K order and zero start), so every value is bit-identical to the one the GEMM
+// folded.  An output element depends only on its A row, its B column and its own accumulator, so
+// the other elements may hold anything: A row i takes chunk row slot 4(i/8) + i%4 (the rows with
+// (i/4)%2 == h are the chunk's, in the GEMM's order) and every B column takes the hidden row.
+// The operands are staged in this wavefront's LDS area (kRcLdsBytes), K segment by K segment, with
+// direct-to-LDS loads: slot s = 4q + r holds the chunk row's segment, slot 16 the hidden row's,
+// kRcSlotBytes apart (16 bytes of padding put the A reads of the 16 slots on distinct banks).  The
+// loads go out piece-major (512 K elements of all 17 rows per piece), so the MFMAs of a piece start
+// as soon as it has landed while the later pieces are still in flight.  Lane l gets the 16 logits
+// of lane (row % 32) + 32h: register r is vocabulary row base32 + 8(r/4) + 4h + r%4.
+constexpr int kRcPieceK = 512;                            // K elements of one row per direct-to-LDS load
+constexpr int kRcPieces = 4;                              // pieces per staged segment
+constexpr int kRcSegK = kRcPieceK * kRcPieces;
+constexpr int kRcSegBytes = kRcSegK * 2;
+constexpr int kRcSlotBytes = kRcSegBytes + 16;
+constexpr int kRcLdsBytes = 17 * kRcSlotBytes;            // 16 chunk rows + the hidden row
+
+__device__ void gemm_chunk_logits(__amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t hrs, int base32, int h, int row,
+                                  int H, uint4* area, float (&zr)[16]) {
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  const int lane = __lane_id();
+  const int i = lane & 31, hk = lane >> 5;
+  const int slot = 4 * (i >> 3) + (i & 3);
+  const unsigned row_bytes = (unsigned)H * 2u;
+  const uint4* a_src = area + (slot * kRcSlotBytes + 16 * hk) / 16;
+  const uint4* b_src = area + (16 * kRcSlotBytes + 16 * hk) / 16;
+  f32x16 acc = f32x16{};
+  uint4 a0[8], b0[8], a1[8], b1[8];
+  auto lds8 = [&](int kg, uint4 (&a)[8], uint4 (&b)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      a[u] = a_src[2 * (kg + u)];
+      b[u] = b_src[2 * (kg + u)];
+    }
+  };
+  auto mma8 = [&](const uint4 (&a)[8], const uint4 (&b)[8]) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = mma32(a[u], b[u], acc);   // (the very first adds to zeros)
+  };
+  for (int seg0 = 0; seg0 < H; seg0 += kRcSegK) {        // (uniform)
+    const int seg_bytes = min(kRcSegK, H - seg0) * 2;     // multiple of 512
+    const int np = (seg_bytes + kRcPieceK * 2 - 1) / (kRcPieceK * 2);
+    __builtin_amdgcn_s_waitcnt(0xc07f);                   // the previous segment's LDS reads are done
+#pragma unroll 1
+    for (int c = 0; c < np; ++c)
+#pragma unroll 1
+      for (int sl = 0; sl < 17; ++sl) {
+        const unsigned r = sl < 16 ? (unsigned)(base32 + 8 * (sl >> 2) + 4 * h + (sl & 3)) : (unsigned)row;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(sl < 16 ? wrs : hrs,
+                                                 (lds_ptr)((char*)area + sl * kRcSlotBytes + c * kRcPieceK * 2), 16,
+                                                 r * row_bytes + (unsigned)(seg0 + c * kRcPieceK) * 2u + 16u * (unsigned)lane,
+                                                 0, 0, 0);
+      }
+#pragma unroll 1
+    for (int c = 0; c < np; ++c) {
+      switch (np - 1 - c) {                               // pieces 0..c have landed (loads retire in order)
+        case 3: wait_vmcnt<3 * 17>(); break;
+        case 2: wait_vmcnt<2 * 17>(); break;
+        case 1: wait_vmcnt<17>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+      const int kg0 = c * (kRcPieceK / 16), kg1 = min(kg0 + kRcPieceK / 16, seg_bytes / 32);   // 16 or 32 K16 steps
+      lds8(kg0, a0, b0);
+      for (int kg = kg0; kg < kg1; kg += 16) {
+        lds8(kg + 8, a1, b1);
+        mma8(a0, b0);
+        if (kg + 16 < kg1) lds8(kg + 16, a0, b0);
+        mma8(a1, b1);
+      }
+    }
+  }
+  const int src_lane = __builtin_amdgcn_readfirstlane((row & 31) + 32 * h);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const float v = acc[rr];
+    zr[rr] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src_lane));
+  }
+}
+
+// The top-k export of one row from its workgroups' chunk lists (one wavefront):
+//   1. the k best chunks of the row: lane l holds lists l, l+64, ... (one per GEMM workgroup), and
+//      kTopK rounds take the best head across the wavefront;
+//   2. the candidates are those chunks' maxima, plus every other token of a chunk whose second
+//      value can reach the k-th chunk maximum T (max - code/8 >= T), recomputed exactly;
+//   3. lanes i < topk write rank i with probability 2^((z - M) log2 e) / S.
+__device__ void gemm_topk_row(const CommitArgs& c, __amdgpu_buffer_rsrc_t tk, int G, int nrows_total, int row, bool rin,
+                              __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t hrs, int H, int V, int id_bits,
+                              float M, float inv_s, uint4* area) {
+  constexpr int N = kMaxVocabGroups / 64;
+  const int lane = __lane_id();
+  const unsigned id_mask = (1u << id_bits) - 1u;
+  uint2 Lst[N][kTopK];
+#pragma unroll
+  for (int n = 0; n < N; ++n) {
+    const int g = lane + 64 * n;
+    const bool in = g < G && rin;
+    const unsigned off = in ? (unsigned)(g * nrows_total + row) * (kTopK * 8u) : 0x80000000u;
+    uint4 e[kTopK / 2];
+#pragma unroll
+    for (int q = 0; q < kTopK / 2; ++q) e[q] = buffer_load16(tk, off == 0x80000000u ? off : off + 16u * q);
+#pragma unroll
+    for (int q = 0; q < kTopK / 2; ++q) {
+      Lst[n][2 * q] = in ? make_uint2(e[q].x, e[q].y) : chunk_empty(id_mask);
+      Lst[n][2 * q + 1] = in ? make_uint2(e[q].z, e[q].w) : chunk_empty(id_mask);
+    }
+  }
+  // 1. the k best chunks, in order (every lane ends with them)
+  uint2 C[kTopK];
+#pragma unroll
+  for (int r = 0; r < kTopK; ++r) {
+    uint2 bh = Lst[0][0];
+    int bn = 0;
+#pragma unroll
+    for (int n = 1; n < N; ++n) {
+      const bool better = chunk_before(Lst[n][0], bh, id_mask);
+      bh = make_uint2(better ? Lst[n][0].x : bh.x, better ? Lst[n][0].y : bh.y);
+      bn = better ? n : bn;
+    }
+    const float m = wave_max(__uint_as_float(bh.x));
+    const int id = wave_allreduce_min(__uint_as_float(bh.x) == m ? (int)(bh.y & id_mask) : (int)id_mask);
+    const bool win = __uint_as_float(bh.x) == m && (int)(bh.y & id_mask) == id && id != (int)id_mask;
+    const uint64_t wl = __builtin_amdgcn_ballot_w64(win);
+    C[r] = chunk_empty(id_mask);
+    if (wl) {
+      const int w = __builtin_ctzll(wl);
+      C[r] = make_uint2(__float_as_uint(m), (unsigned)__builtin_amdgcn_readlane((int)bh.y, w));
+    }
+    if (win) {
+#pragma unroll
+      for (int n = 0; n < N; ++n)
+        if (n == bn) {
+#pragma unroll
+          for (int i = 0; i < kTopK - 1; ++i) Lst[n][i] = Lst[n][i + 1];
+          Lst[n][kTopK - 1] = chunk_empty(id_mask);
+        }
+    }
+  }
+  // 2. the candidates: the chunk maxima, best first, then the recomputed chunks' other tokens
+  uint2 F[kTopK];
+#pragma unroll
+  for (int i = 0; i < kTopK; ++i) F[i] = make_uint2(C[i].x, C[i].y & id_mask);
+  const float T = __uint_as_float(C[kTopK - 1].x);
+  for (int i = 0; i < kTopK; ++i) {
+    uint2 ci = C[0];                                      // (selects: no indexing by a variable)
+#pragma unroll
+    for (int k = 1; k < kTopK; ++k) ci = make_uint2(i == k ? C[k].x : ci.x, i == k ? C[k].y : ci.y);
+    const float zc = __uint_as_float((unsigned)__builtin_amdgcn_readfirstlane((int)ci.x));
+    const unsigned idc = (unsigned)__builtin_amdgcn_readfirstlane((int)ci.y);
+    const bool recompute = zc > -INFINITY && zc - chunk_gap_bound(idc >> id_bits, id_bits) >= T;
+    if (!recompute) continue;                             // (uniform)
+    const int id1 = (int)(idc & id_mask);
+    const int base32 = id1 & ~31, h = (id1 >> 2) & 1;
+    float zr[16];                                         // the chunk's 16 logits, in every lane
+    gemm_chunk_logits(wrs, hrs, base32, h, row, H, area, zr);
+#pragma unroll 1
+    for (int rr = 0; rr < 16; ++rr) {
+      const int v = base32 + 8 * (rr >> 2) + 4 * h + (rr & 3);
+      float zv = zr[0];
+#pragma unroll
+      for (int q = 1; q < 16; ++q) zv = rr == q ? zr[q] : zv;
+      uint2 carry = make_uint2(__float_as_uint(zv), (unsigned)v);
+      if (v >= V || v == id1 || !chunk_before(carry, F[kTopK - 1], id_mask)) continue;   // (uniform)
+#pragma unroll
+      for (int k = 0; k < kTopK; ++k) {
+        const bool b = chunk_before(carry, F[k], id_mask);
+        const uint2 e = F[k];
+        F[k] = make_uint2(b ? carry.x : e.x, b ? carry.y : e.y);
+        carry = make_uint2(b ? e.x : carry.x, b ? e.y : carry.y);
+      }
+    }
+  }
+  // 3. the export: lane i writes rank i
+  if (rin && lane < c.topk) {
+    uint2 e = F[0];
+#pragma unroll
+    for (int i = 1; i < kTopK; ++i) e = make_uint2(lane == i ? F[i].x : e.x, lane == i ? F[i].y : e.y);
+    const bool real = e.y != id_mask;
+    const size_t o = (size_t)row * c.topk + lane;
+    c.out_topk_tokens[o] = real ? (int)e.y : -1;
+    if (c.out_topk_prob) c.out_topk_prob[o] = real ? fminf(ex2((__uint_as_float(e.x) - M) * kLog2e) * inv_s, 1.f) : 0.f;
+  }
+}
+
+struct GemmTopkArgs {           // the export's inputs on the GEMM path (TK finalizer only)
+  const uint4* lists;           // [G][nrows_total] chunk lists of gemm_r512_topk_kernel
+  const void* W;                // [V][H] bf16
+  const void* hidden;           // [M][H] bf16, the step's hidden rows
+  int H, V;
+  int id_bits;                  // bit length of V (the chunk entries' id field)
+};
+
+template <bool TK>
 __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c, const float4* records, int G,
-                                                             int nrows_total, unsigned* tickets,
-                                                             float4* row_out) {
+                                                             int nrows_total, unsigned* tickets, float4* row_out,
+                                                             const GemmTopkArgs tka) {
   constexpr unsigned kOOB = 0x80000000u;
-  const int parts = (c.L + kFinRows - 1) / kFinRows;
+  constexpr int kRows = TK ? kFinRowsTopk : kFinRows;
+  const int parts = (c.L + kRows - 1) / kRows;
   const int b = gid() / parts, part = gid() % parts;
   const int tid = lid(), lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bool do_commit = (c.flags & kFlagCommit) != 0;
   const __amdgpu_buffer_rsrc_t rec =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<float4*>(records), 0, nrows_total * G * 16, 0x00020000);
-  const int r = part * kFinRows + wave * 4 + (lane >> 4);   // row within the sequence
+  const int r = part * kRows + (TK ? wave : wave * 4 + (lane >> 4));   // row within the sequence
   const bool rin = r < c.L;
   const int row = b * c.L + (rin ? r : 0);
   const int j = lane & 15;
+  const bool writer = TK ? lane == 0 : j == 0;              // one lane per row writes its outputs
   Stats t;
   if (G <= kGroup) {
     const float4 v = record_load_after_kernel(rec, j < G && rin ? 16u * (unsigned)(row + j * nrows_total) : kOOB);
@@ -1532,8 +1850,19 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
   }
   // S >= 1 in exact arithmetic; the rounding of m*log2(e) may put 1/S a few ulps above 1
   const float conf = fminf(1.f / t.s, 1.f), gap = t.m1 - t.m2;
+  if constexpr (TK) {
+    const __amdgpu_buffer_rsrc_t wrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(tka.W), 0, (int)((unsigned)tka.V * (unsigned)tka.H * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(tka.hidden), 0, (int)((unsigned)(c.B * c.L) * (unsigned)tka.H * 2u), 0x00020000);
+    const __amdgpu_buffer_rsrc_t tk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint4*>(tka.lists), 0, nrows_total * G * (kTopK * 8), 0x00020000);
+    __shared__ uint4 rc_area[TK ? kFinRowsTopk * kRcLdsBytes / 16 : 1];   // a recompute area per wavefront
+    gemm_topk_row(c, tk, G, nrows_total, row, rin, wrs, hrs, tka.H, tka.V, tka.id_bits, t.m1, 1.f / t.s,
+                  rc_area + (TK ? wave * (kRcLdsBytes / 16) : 0));
+  }
   if (!do_commit) {
-    if (rin && j == 0) {
+    if (rin && writer) {
       if (c.out_records) {                                // vocabulary shard: the merged record
         Stats o = t;
         o.id = t.id + c.v_begin;
@@ -1547,7 +1876,7 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
     return;
   }
   const __amdgpu_buffer_rsrc_t out = __builtin_amdgcn_make_buffer_rsrc(row_out, 0, c.B * c.L * 16, 0x00020000);
-  if (rin && j == 0) record_store(out, 16u * (unsigned)row, make_float4(conf, __int_as_float(t.id), gap, 0.f));
+  if (rin && writer) record_store(out, 16u * (unsigned)row, make_float4(conf, __int_as_float(t.id), gap, 0.f));
   __builtin_amdgcn_s_waitcnt(0);                          // published before this part is counted
   __syncthreads();
   __shared__ int s_last;

@@ -205,16 +205,20 @@ def test_decode_steps_validation():
 
 
 def test_topk_workspace_sizes():
-    # top-k on: the streaming plan for every shape, plus one list of 8 (logit, id) pairs (64 bytes)
-    # per (padded row, vocabulary range) after the statistics records, then one merged list per
-    # (padded row, group of 16 ranges)
+    # top-k on, streaming plan (up to 64 rows, or float32): one list of 8 (logit, id) pairs (64
+    # bytes) per (padded row, vocabulary range) after the statistics records, then one merged list
+    # per (padded row, group of 16 ranges)
     base = 256 + 32 * 256 * 16 + 32 * 16 * 16
     assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 8) == base + 32 * 256 * 64 + 32 * 16 * 64
     assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 3) == base + 32 * 256 * 64 + 32 * 16 * 64
-    # 512 bf16 rows: 64-row groups (8 of them), 32 vocabulary ranges (2 groups) each, no packed
-    # hidden rows
+    assert nat.dlm_workspace_bytes_topk(8, 32, 256, 20011, nat.DLM_F32, 8) == \
+        256 + 256 * 64 * 16 + 256 * 4 * 16 + 256 * 64 * 64 + 256 * 4 * 64   # 4 groups of 64 rows, 64 ranges
+    # GEMM-shaped plan beyond 64 bf16 rows: always the 512-row group shape; after the plain GEMM
+    # workspace, one list of 8 chunk entries (64 bytes) per (padded row, workgroup)
     assert nat.dlm_workspace_bytes_topk(16, 32, 2048, 157184, nat.DLM_BF16, 8) == \
-        256 + 512 * 32 * 16 + 512 * 2 * 16 + 512 * 32 * 64 + 512 * 2 * 64
+        nat.dlm_workspace_bytes(16, 32, 2048, 157184, nat.DLM_BF16) + 512 * 256 * 64
+    assert nat.dlm_workspace_bytes_topk(5, 13, 256, 3001, nat.DLM_BF16, 8) == \
+        256 + 512 * 24 * 16 + 96 * 256 * 2 + 65 * 16 + 512 * 24 * 64     # 24 tiles of 128: 24 workgroups
     for B, L, H, V, dt in [(1, 32, 2048, 126464, 1), (16, 32, 2048, 157184, 1), (1, 8, 64, 1024, 0)]:
         assert nat.dlm_workspace_bytes_topk(B, L, H, V, dt, 0) == nat.dlm_workspace_bytes(B, L, H, V, dt)
     assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 9) == 0

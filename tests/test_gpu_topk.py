@@ -88,7 +88,11 @@ def _valid(tok, prob, V, k):
     (1, 3, 64, 1, "bf16", 3),              # one-token vocabulary
     (3, 40, 4096, 5003, "bf16", 4),        # 16 K fragments per wavefront, two 16-row blocks per group
     (5, 20, 128, 20011, "f32", 8),         # four 16-row blocks per group
-    (16, 32, 2048, 30011, "bf16", 8),      # 512 rows: the streaming head with the fold, 8 row groups
+    (16, 32, 2048, 30011, "bf16", 8),      # 512 rows: the GEMM-shaped head's chunk lists, ragged tile
+    (16, 32, 2048, 157184, "bf16", 8),     # the batched workload's shape: GEMM-shaped head, no partial tile
+    (5, 13, 256, 3001, "bf16", 8),         # 65 rows on the GEMM-shaped head (512-row group, mostly padding)
+    (3, 32, 256, 5, "bf16", 8),            # fewer tokens than k on the GEMM-shaped head
+    (8, 32, 256, 20011, "f32", 6),         # 256 float32 rows: the streaming head with the fold
 ])
 def test_topk_token_stats(B, L, H, V, dtype, k):
     from decoding_step_amd import _native as nat
@@ -132,6 +136,36 @@ def test_topk_exact_ties_across_workgroups():
         assert tok[r] == 5 and gap[r] == 0.0
     ref = oracle.topk_candidates(h.astype(np.float32), W, 8)
     assert ref["tok"][:, :7].tolist() == [want, want]
+
+
+def test_topk_gemm_head_ties_inside_one_chunk():
+    """GEMM-shaped head (96 rows): a row whose best tokens share one chunk (a lane's 16 ids of one
+    32-row vocabulary block) must be recomputed exactly, and exact ties (copied rows, in the same
+    chunk and in other chunks) must come out adjacent and in id order with equal probabilities."""
+    from decoding_step_amd import _native as nat
+    from decoding_step_amd.synth import BlockStream, bf16_bits, bf16_to_f32, make_weights
+    B, L, H, V, k = 3, 32, 256, 4096, 8
+    say(f"gpu: top-k ties inside a chunk, GEMM-shaped head B={B} L={L} V={V}")
+    W = make_weights(V, H, "bf16", seed=9)
+    a, b, c = 65, 73, 2000                # a and b: ids 64 + {1, 9}, both in half 0 of block 64..95
+    W[b] = W[a]
+    W[c] = W[a]
+    h = BlockStream(W, B * L, 77, 30.0).hidden(0, 0)
+    wa = bf16_to_f32(W[a])
+    h[0] = bf16_bits(wa * 8.0)            # a, b, c tie far ahead of every other token
+    w2 = bf16_to_f32(W[a + 2])            # id 67: same chunk as a and b
+    h[1] = bf16_bits(wa * 6.0 + w2 * 6.0)
+    conf, tok, gap, tt, tp = _stats_topk(h, W, B, L, k, nat.DLM_BF16)
+    _valid(tt, tp, V, k)
+    assert np.array_equal(tt[:, 0], tok) and np.array_equal(tp[:, 0], conf)
+    assert tt[0, :3].tolist() == [a, b, c], tt[0]
+    assert tp[0, 0] == tp[0, 1] == tp[0, 2]
+    ref = oracle.topk_candidates(h[:2], W, k)
+    assert ref["tok"][0, :3].tolist() == [a, b, c]
+    rows = np.arange(B * L)
+    compared, exempt = _check_against_oracle(h, W, rows, k, tt, tp)
+    say(f"[top-k ties] {compared} ranks compared exactly, {exempt} near-ties")
+    assert compared >= len(rows) * 4
 
 
 def _plain_and_topk_steps(name, k, n_steps):
@@ -189,10 +223,23 @@ def test_topk_leaves_the_step_unchanged(name):
 
 
 def test_topk_step_on_the_batched_workload():
-    """512 rows: the step with top-k takes the streaming head instead of the GEMM-shaped one;
-    commits are checked against the oracle on sampled sequences (near-tie rules as elsewhere)."""
+    """512 rows: the step with top-k runs the GEMM-shaped head with its chunk lists; statistics,
+    commits and state must equal the plain step's bit for bit, commits are checked against the
+    oracle on sampled sequences (near-tie rules as elsewhere), the export on sampled rows."""
+    from decoding_step_amd.device import credit_tokens, credit_values
     say("gpu: step with top-k, mixed_b16_l32")
-    for wl, W, seq, h, plain, withk, m1, m2, c1, c2 in _plain_and_topk_steps("mixed_b16_l32", 8, 1):
+    first_done = False
+    for wl, W, seq, h, plain, withk, m1, m2, c1, c2 in _plain_and_topk_steps("mixed_b16_l32", 8, 2):
+        assert np.array_equal(plain.out_tokens.cpu().numpy(), withk.out_tokens.cpu().numpy())
+        assert np.array_equal(plain.out_commit.cpu().numpy(), withk.out_commit.cpu().numpy())
+        assert np.array_equal(plain.conf.cpu().numpy(), withk.conf.cpu().numpy())
+        assert np.array_equal(plain.gap.cpu().numpy(), withk.gap.cpu().numpy())
+        assert np.array_equal(m1, m2)
+        assert np.array_equal(credit_tokens(c1).cpu().numpy(), credit_tokens(c2).cpu().numpy())
+        assert np.array_equal(credit_values(c1).cpu().numpy(), credit_values(c2).cpu().numpy())
+        if first_done:
+            continue                       # the oracle check below starts from fresh blocks: first step only
+        first_done = True
         sample = [0, 5, 9, 15]
         ref = oracle.decode_step(h[sample], oracle.as_f64(W), np.ones((len(sample), wl.L), np.uint8),
                                  [seq[b] for b in sample], auto_advance=True)
