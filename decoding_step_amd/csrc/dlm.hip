@@ -293,9 +293,9 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   hipStream_t stream = static_cast<hipStream_t>(pol->stream);
   if (p.gemm) {
     void* packed = static_cast<char*>(pol->workspace) + p.packed_off;
-    const int pack_blocks = (int)std::min<size_t>((p.packed_bytes / 16 + 255) / 256, 1024);
-    hipLaunchKernelGGL(dlm::pack_hidden_kernel, dim3(pack_blocks), dim3(256), 0, stream,
-                       static_cast<const uint4*>(hidden), static_cast<uint4*>(packed), a.M, a.H, pack_blocks * 256);
+    const int pack_waves = (a.M + 31) / 32 * (a.H / 64);   // (H % 256 == 0 on this path)
+    hipLaunchKernelGGL(dlm::pack_hidden_kernel, dim3((pack_waves + 3) / 4), dim3(256), 0, stream,
+                       static_cast<const uint4*>(hidden), static_cast<uint4*>(packed), a.M, a.H);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "pack kernel launch: %s", hipGetErrorString(e));
     dlm::GemmArgs g;

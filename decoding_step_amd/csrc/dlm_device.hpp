@@ -1241,18 +1241,28 @@ __device__ __forceinline__ uint2 chunk_empty(unsigned id_mask) { return make_uin
 
 // Hidden rows -> MFMA fragment order: fragment (rb, kg) is 1 KB at (rb * H/16 + kg) * 1 KB, lane l
 // holding row 32rb + l%32, elements 16kg + 8(l/32) .. +8.  Rows past M are zero.
-__global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4* hp, int M, int H, int nthreads) {
+// Fragment (rb, kg) of the packed hidden rows is 1 KB: lane l's 16 bytes are K elements
+// 16kg + 8(l/32) .. +7 of row 32rb + l%32 (zeros past M).  One wavefront packs four consecutive
+// fragments of one 32-row block: each of its four loads covers 8 rows x 128 contiguous bytes, and
+// each store writes 8 whole 128-byte lines of the output (lanes l%8 == u, 8 rows apart).
+// Grid: ceil(M/32) * H/64 wavefronts, four per workgroup (H % 64 == 0).
+__global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4* hp, int M, int H) {
   const int KG = H / 16;
-  const size_t n = (size_t)((M + 31) / 32) * KG * 64;
-  const size_t stride = (size_t)nthreads;
-  for (size_t i = (size_t)gid() * 256 + lid(); i < n; i += stride) {
-    const int l = (int)(i & 63);
-    const size_t f = i >> 6;
-    const int kg = (int)(f % KG), rb = (int)(f / KG);
-    const int row = 32 * rb + (l & 31);
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (row < M) v = h[(size_t)row * (H / 8) + 2 * kg + (l >> 5)];
-    hp[i] = v;
+  const int w = gid() * 4 + (lid() >> 6), lane = lid() & 63;
+  const int quads = KG / 4;
+  if (w >= ((M + 31) / 32) * quads) return;
+  const int rb = w / quads, kg0 = 4 * (w % quads);
+  const int u = lane & 7;                                 // 16-byte unit of the row's 128 bytes
+  uint4 v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 32 * rb + 8 * j + (lane >> 3);
+    v[j] = row < M ? h[(unsigned)row * (unsigned)(H / 8) + (unsigned)(2 * kg0 + u)] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 8 * j + (lane >> 3);
+    hp[((unsigned)(rb * KG + kg0 + (u >> 1)) << 6) + (unsigned)(i + 32 * (u & 1))] = v[j];
   }
 }
 
