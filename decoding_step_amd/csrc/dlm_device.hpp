@@ -1239,10 +1239,9 @@ __device__ __forceinline__ bool chunk_before(uint2 a, uint2 b, unsigned id_mask)
 
 __device__ __forceinline__ uint2 chunk_empty(unsigned id_mask) { return make_uint2(__float_as_uint(-INFINITY), id_mask); }
 
-// Hidden rows -> MFMA fragment order: fragment (rb, kg) is 1 KB at (rb * H/16 + kg) * 1 KB, lane l
-// holding row 32rb + l%32, elements 16kg + 8(l/32) .. +8.  Rows past M are zero.
-// Fragment (rb, kg) of the packed hidden rows is 1 KB: lane l's 16 bytes are K elements
-// 16kg + 8(l/32) .. +7 of row 32rb + l%32 (zeros past M).  One wavefront packs four consecutive
+// Hidden rows -> MFMA fragment order.  Fragment (rb, kg) of the packed rows is 1 KB: lane l's
+// 16 bytes are K elements 16kg + 8(l/32) .. +7 of row 32rb + l%32 (zeros past M), at
+// (rb * H/16 + kg) * 1 KB.  One wavefront packs four consecutive
 // fragments of one 32-row block: each of its four loads covers 8 rows x 128 contiguous bytes, and
 // each store writes 8 whole 128-byte lines of the output (lanes l%8 == u, 8 rows apart).
 // Grid: ceil(M/32) * H/64 wavefronts, four per workgroup (H % 64 == 0).
@@ -1638,14 +1637,14 @@ constexpr int kFinRowsTopk = 2;   // with the top-k export: one row per wavefron
 // the other elements may hold anything: A row i takes chunk row slot 4(i/8) + i%4 (the rows with
 // (i/4)%2 == h are the chunk's, in the GEMM's order) and every B column takes the hidden row.
 // The operands are staged in this wavefront's LDS area (kRcLdsBytes), K segment by K segment, with
-// direct-to-LDS loads: slot s = 4q + r holds the chunk row's segment, slot 16 the hidden row's,
-// kRcSlotBytes apart (16 bytes of padding put the A reads of the 16 slots on distinct banks).  The
-// loads go out piece-major (512 K elements of all 17 rows per piece), so the MFMAs of a piece start
-// as soon as it has landed while the later pieces are still in flight.  Lane l gets the 16 logits
-// of lane (row % 32) + 32h: register r is vocabulary row base32 + 8(r/4) + 4h + r%4.
+// direct-to-LDS loads, all in flight at once: slot s = 4q + r holds the chunk row's segment, slot
+// 16 the hidden row's, kRcSlotBytes apart (16 bytes of padding put the A reads of the 16 slots on
+// distinct banks).  (The compiler cannot tell which direct-to-LDS load an LDS read depends on, so
+// it waits for all of them before the first read anyway.)  The operand reads of the next eight
+// MFMAs go out before the current eight.  Lane l gets the 16 logits of lane (row % 32) + 32h:
+// register r is vocabulary row base32 + 8(r/4) + 4h + r%4.
 constexpr int kRcPieceK = 512;                            // K elements of one row per direct-to-LDS load
-constexpr int kRcPieces = 4;                              // pieces per staged segment
-constexpr int kRcSegK = kRcPieceK * kRcPieces;
+constexpr int kRcSegK = 2048;                             // K elements staged at a time
 constexpr int kRcSegBytes = kRcSegK * 2;
 constexpr int kRcSlotBytes = kRcSegBytes + 16;
 constexpr int kRcLdsBytes = 17 * kRcSlotBytes;            // 16 chunk rows + the hidden row
@@ -1677,31 +1676,23 @@ __device__ void gemm_chunk_logits(__amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rs
     const int np = (seg_bytes + kRcPieceK * 2 - 1) / (kRcPieceK * 2);
     __builtin_amdgcn_s_waitcnt(0xc07f);                   // the previous segment's LDS reads are done
 #pragma unroll 1
-    for (int c = 0; c < np; ++c)
+    for (int sl = 0; sl < 17; ++sl) {
+      const unsigned r = sl < 16 ? (unsigned)(base32 + 8 * (sl >> 2) + 4 * h + (sl & 3)) : (unsigned)row;
 #pragma unroll 1
-      for (int sl = 0; sl < 17; ++sl) {
-        const unsigned r = sl < 16 ? (unsigned)(base32 + 8 * (sl >> 2) + 4 * h + (sl & 3)) : (unsigned)row;
+      for (int c = 0; c < np; ++c)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(sl < 16 ? wrs : hrs,
                                                  (lds_ptr)((char*)area + sl * kRcSlotBytes + c * kRcPieceK * 2), 16,
                                                  r * row_bytes + (unsigned)(seg0 + c * kRcPieceK) * 2u + 16u * (unsigned)lane,
                                                  0, 0, 0);
-      }
-#pragma unroll 1
-    for (int c = 0; c < np; ++c) {
-      switch (np - 1 - c) {                               // pieces 0..c have landed (loads retire in order)
-        case 3: wait_vmcnt<3 * 17>(); break;
-        case 2: wait_vmcnt<2 * 17>(); break;
-        case 1: wait_vmcnt<17>(); break;
-        default: wait_vmcnt<0>(); break;
-      }
-      const int kg0 = c * (kRcPieceK / 16), kg1 = min(kg0 + kRcPieceK / 16, seg_bytes / 32);   // 16 or 32 K16 steps
-      lds8(kg0, a0, b0);
-      for (int kg = kg0; kg < kg1; kg += 16) {
-        lds8(kg + 8, a1, b1);
-        mma8(a0, b0);
-        if (kg + 16 < kg1) lds8(kg + 16, a0, b0);
-        mma8(a1, b1);
-      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);                        // (vmcnt: the direct-to-LDS loads have landed)
+    const int kgs = seg_bytes / 32;                       // K16 steps: a multiple of 16
+    lds8(0, a0, b0);
+    for (int kg = 0; kg < kgs; kg += 16) {
+      lds8(kg + 8, a1, b1);
+      mma8(a0, b0);
+      if (kg + 16 < kgs) lds8(kg + 16, a0, b0);
+      mma8(a1, b1);
     }
   }
   const int src_lane = __builtin_amdgcn_readfirstlane((row & 31) + 32 * h);
@@ -1716,7 +1707,8 @@ __device__ void gemm_chunk_logits(__amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rs
 //   1. the k best chunks of the row: lane l holds lists l, l+64, ... (one per GEMM workgroup), and
 //      kTopK rounds take the best head across the wavefront;
 //   2. the candidates are those chunks' maxima, plus every other token of a chunk whose second
-//      value can reach the k-th chunk maximum T (max - code/8 >= T), recomputed exactly;
+//      value can reach the k-th chunk maximum T (maximum - bound(gap code) >= T), recomputed
+//      exactly, best first; a recomputed token enters only above the current k-th candidate;
 //   3. lanes i < topk write rank i with probability 2^((z - M) log2 e) / S.
 __device__ void gemm_topk_row(const CommitArgs& c, __amdgpu_buffer_rsrc_t tk, int G, int nrows_total, int row, bool rin,
                               __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t hrs, int H, int V, int id_bits,

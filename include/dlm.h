@@ -39,7 +39,7 @@
 extern "C" {
 #endif
 
-#define DLM_VERSION_STRING "0.5.0"
+#define DLM_VERSION_STRING "0.6.0"
 
 #define DLM_MAX_SEQS 256   /* sequences per call                                  */
 #define DLM_MAX_L 64       /* positions per block: one wavefront lane per position */
@@ -150,11 +150,14 @@ typedef struct {
  *   out_topk_prob[r][i]    its softmax probability over the whole vocabulary,
  *                          exp(z - max z) / sum_v exp(z_v - max z), so entry 0 is the confidence;
  *   entries past V         token -1, probability 0.
- * The workspace must hold dlm_workspace_bytes_topk(B, L, H, V, dtype, topk) bytes.  With top-k
- * on, every shape takes the streaming LM head (one kernel: the lists are merged with the
- * statistics).  Errors: topk outside 0..DLM_MAX_TOPK gives
- * DLM_ERR_POLICY, topk > 0 with out_topk_tokens NULL gives DLM_ERR_NULL, a workspace smaller
- * than the top-k size gives DLM_ERR_WORKSPACE.
+ * The workspace must hold dlm_workspace_bytes_topk(B, L, H, V, dtype, topk) bytes.  Up to 64
+ * rows (and in float32) the streaming LM head folds the lists next to the statistics in its one
+ * kernel.  Beyond 64 bfloat16 rows with H % 256 == 0 and V < 2^22 the GEMM-shaped head keeps,
+ * per row, lists of its best 16-logit chunks, and the finalizer recomputes (bit-identically) the
+ * rare chunk that may hold a second top-k token; the extra workspace there is 64 bytes per row
+ * (rows padded to the 512-row group) and GEMM workgroup: 8 MiB at 512 rows.
+ * Errors: topk outside 0..DLM_MAX_TOPK gives DLM_ERR_POLICY, topk > 0 with out_topk_tokens NULL
+ * gives DLM_ERR_NULL, a workspace smaller than the top-k size gives DLM_ERR_WORKSPACE.
  */
 
 /*
@@ -189,7 +192,7 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
  *     Shapes that need more than DLM_NOALLOC_SCRATCH_BYTES in that layout (the workspace of
  *     dlm_decode_step / dlm_workspace_bytes_topk plus at most 8 KB) give DLM_ERR_WORKSPACE
  *     before anything is enqueued.  Blocks of up to 16 x 32 rows at V = 157184, H = 2048 fit
- *     (about 3.2 MB), with or without the top-k export at one sequence.
+ *     without the top-k export (about 3.2 MB), and one sequence of 32 rows with it.
  *   - The call allocates and frees nothing.  The first call on a device looks up that device's
  *     copy of the array and enqueues a fill kernel on `stream` that zeroes its counter region;
  *     every call leaves the counters at zero again, so calls of different shapes may follow one
