@@ -362,7 +362,8 @@ def main():
             "roofline": {"bound": "hbm", "kernel": "dlm_shard_stats (shard-shaped LM head)",
                          "achieved": shard_bytes / (t_shard / args.steps) / 1e9, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": shard_bytes / (t_shard / args.steps) / 1e9 / HBM_PEAK_GBS,
-                         "traffic": None, "algorithmic_bytes_per_launch": shard_bytes},
+                         "traffic": measured_traffic(f"{wl.name}_shard{args.shards}"),
+                         "algorithmic_bytes_per_launch": shard_bytes},
             "shard_us": t_shard / args.steps * 1e6, "merge_commit_us": t_merge / args.steps * 1e6,
             "cpu_baseline": None,
         }

@@ -55,20 +55,22 @@ def mean(xs):
     return sum(xs) / len(xs)
 
 
-def summarize(workload, kernel, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes):
+def summarize(workload, kernel, fetch_dir, write_dir, copy_fetch_dir, copy_write_dir, copy_bytes, skip=0):
     cf = mean(counter_values(copy_fetch_dir, "FETCH_SIZE", COPY_KERNEL))
     cw = mean(counter_values(copy_write_dir, "WRITE_SIZE", COPY_KERNEL))
     fetch_scale = copy_bytes / (cf * 1024.0)
     write_scale = copy_bytes / (cw * 1024.0)
-    kf = counter_values(fetch_dir, "FETCH_SIZE", kernel)
-    kw = counter_values(write_dir, "WRITE_SIZE", kernel)
+    kf = counter_values(fetch_dir, "FETCH_SIZE", kernel)[skip:]
+    kw = counter_values(write_dir, "WRITE_SIZE", kernel)[skip:]
+    if not kf or not kw:
+        raise ValueError(f"no dispatches of {kernel!r} left after skipping {skip}")
     rd = mean(kf) * 1024.0 * fetch_scale
     wr = mean(kw) * 1024.0 * write_scale
     return {
         "kernel": kernel,
         "workload": workload,
         "kernel_source_sha256": kernel_source_hash(),
-        "dispatches": {"fetch": len(kf), "write": len(kw)},
+        "dispatches": {"fetch": len(kf), "write": len(kw), "skipped": skip},
         "fetch_size_kib_per_dispatch": round(mean(kf), 1),
         "write_size_kib_per_dispatch": round(mean(kw), 1),
         "copy_calibration": {"bytes_per_copy": copy_bytes, "fetch_size_kib": round(cf, 1),
@@ -89,9 +91,12 @@ def main():
     ap.add_argument("--copy-fetch", required=True)
     ap.add_argument("--copy-write", required=True)
     ap.add_argument("--copy-mib", type=int, default=512)
+    ap.add_argument("--skip", type=int, default=0,
+                    help="leave out the first N matching dispatches (e.g. the whole-vocabulary launches "
+                         "that record the trajectory before a shard run)")
     ap.add_argument("--out", default=None)
     a = ap.parse_args()
-    d = summarize(a.workload, a.kernel, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib << 20)
+    d = summarize(a.workload, a.kernel, a.fetch, a.write, a.copy_fetch, a.copy_write, a.copy_mib << 20, a.skip)
     out = a.out or os.path.join(ROOT, "profiles", f"{a.workload}_counters.json")
     with open(out, "w") as f:
         json.dump(d, f, indent=1)
