@@ -192,7 +192,7 @@ int dlm_decode_step(const void* hidden, const void* W_vocab, uint8_t* mask_state
  *     Shapes that need more than DLM_NOALLOC_SCRATCH_BYTES in that layout (the workspace of
  *     dlm_decode_step / dlm_workspace_bytes_topk plus at most 8 KB) give DLM_ERR_WORKSPACE
  *     before anything is enqueued.  Blocks of up to 16 x 32 rows at V = 157184, H = 2048 fit
- *     without the top-k export (about 3.2 MB), and one sequence of 32 rows with it.
+ *     without the top-k export (4.2 MB), and one sequence of 32 rows with it (0.7 MB).
  *   - The call allocates and frees nothing.  The first call on a device looks up that device's
  *     copy of the array and enqueues a fill kernel on `stream` that zeroes its counter region;
  *     every call leaves the counters at zero again, so calls of different shapes may follow one
