@@ -382,6 +382,18 @@ __device__ __forceinline__ Stats stats_unpack(const float4& v) {
   return t;
 }
 
+// The record, or the empty statistics where `in` is false, by one select per field: a select of
+// whole structs became a branch around the record's use, the compiler then moved the load into
+// that branch, and a load issued on a branch makes every later wait a wait for all loads.
+__device__ __forceinline__ Stats stats_unpack_if(const float4& v, bool in) {
+  Stats t;
+  t.m1 = in ? v.x : -INFINITY;
+  t.s = in ? v.y : 0.f;
+  t.id = in ? __float_as_int(v.z) : 0x7fffffff;
+  t.m2 = in ? v.w : -INFINITY;
+  return t;
+}
+
 // Fold one logit z of id v (ids arrive in ascending order per thread) into the running stats.
 __device__ __forceinline__ void stats_fold1(Stats& st, float z, int v) {
   const float mnew = fmaxf(st.m1, z);
@@ -757,7 +769,7 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
         }
         Stats q[kGroup];
 #pragma unroll
-        for (int k = 0; k < kGroup; ++k) q[k] = kGroup * j + k < G ? stats_unpack(v[k]) : stats_empty();
+        for (int k = 0; k < kGroup; ++k) q[k] = stats_unpack_if(v[k], kGroup * j + k < G);
         t = stats_row16_merge(stats_tree(q));
       }
       if (rin && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
@@ -1425,12 +1437,15 @@ __device__ __forceinline__ void gemm_stats(const GemmArgs& a) {
     return __builtin_amdgcn_readfirstlane(
         s < total ? (unsigned)((gi + ti * a.G_t) * G::BN) * row_bytes + (unsigned)(kk * kGemmBK * 2) : kOOB);
   };
+  // W is read once: the loads carry the non-temporal policy (cache policy bit 1, nt), so W lines
+  // leave the L2 first and the packed hidden rows, which every workgroup of the XCD re-reads per
+  // tile, stay (HBM fetch 1.13x -> 1.05x the algorithmic bytes)
   auto w_issue = [&](int slot, unsigned soff) {
 #pragma unroll
     for (int i = 0; i < G::WDma; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           wrs, (__attribute__((address_space(3))) void*)(ring(slot) + (8 * G::WDma * wave + 8 * i) * 8), 16,
-          w_voff[i], soff, 0, 0);
+          w_voff[i], soff, 0, 2);
   };
   // fragment reads: lane l, block vb, K16 step ks reads tile row r = 32vb + l%32, chunk
   // c = 2ks + l/32, at slot r*8 + (c ^ swz(r)) = 256vb + 8(l%32) + (x_l ^ 2(ks ^ 2(vb&1))) with
@@ -1710,25 +1725,36 @@ __device__ void gemm_chunk_logits(__amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rs
 //      value can reach the k-th chunk maximum T (maximum - bound(gap code) >= T), recomputed
 //      exactly, best first; a recomputed token enters only above the current k-th candidate;
 //   3. lanes i < topk write rank i with probability 2^((z - M) log2 e) / S.
-__device__ void gemm_topk_row(const CommitArgs& c, __amdgpu_buffer_rsrc_t tk, int G, int nrows_total, int row, bool rin,
-                              __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t hrs, int H, int V, int id_bits,
-                              float M, float inv_s, uint4* area) {
-  constexpr int N = kMaxVocabGroups / 64;
+constexpr int kTopkListsPerLane = kMaxVocabGroups / 64;
+
+// This lane's chunk lists of the row (lists lane, lane + 64, ...; past G: out of range, zeros).
+// Issued beside the row's statistics records, so both arrive in one round trip.
+__device__ __forceinline__ void gemm_topk_load(__amdgpu_buffer_rsrc_t tk, int G, int nrows_total, int row, bool rin,
+                                               uint4 (&e)[kTopkListsPerLane][kTopK / 2]) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int n = 0; n < kTopkListsPerLane; ++n) {
+    const int g = lane + 64 * n;
+    const unsigned off = g < G && rin ? (unsigned)(g * nrows_total + row) * (kTopK * 8u) : 0x80000000u;
+#pragma unroll
+    for (int q = 0; q < kTopK / 2; ++q) e[n][q] = buffer_load16(tk, off == 0x80000000u ? off : off + 16u * q);
+  }
+}
+
+__device__ void gemm_topk_row(const CommitArgs& c, const uint4 (&e)[kTopkListsPerLane][kTopK / 2], int G, int row,
+                              bool rin, __amdgpu_buffer_rsrc_t wrs, __amdgpu_buffer_rsrc_t hrs, int H, int V,
+                              int id_bits, float M, float inv_s, uint4* area) {
+  constexpr int N = kTopkListsPerLane;
   const int lane = __lane_id();
   const unsigned id_mask = (1u << id_bits) - 1u;
   uint2 Lst[N][kTopK];
 #pragma unroll
   for (int n = 0; n < N; ++n) {
-    const int g = lane + 64 * n;
-    const bool in = g < G && rin;
-    const unsigned off = in ? (unsigned)(g * nrows_total + row) * (kTopK * 8u) : 0x80000000u;
-    uint4 e[kTopK / 2];
-#pragma unroll
-    for (int q = 0; q < kTopK / 2; ++q) e[q] = buffer_load16(tk, off == 0x80000000u ? off : off + 16u * q);
+    const bool in = lane + 64 * n < G && rin;
 #pragma unroll
     for (int q = 0; q < kTopK / 2; ++q) {
-      Lst[n][2 * q] = in ? make_uint2(e[q].x, e[q].y) : chunk_empty(id_mask);
-      Lst[n][2 * q + 1] = in ? make_uint2(e[q].z, e[q].w) : chunk_empty(id_mask);
+      Lst[n][2 * q] = in ? make_uint2(e[n][q].x, e[n][q].y) : chunk_empty(id_mask);
+      Lst[n][2 * q + 1] = in ? make_uint2(e[n][q].z, e[n][q].w) : chunk_empty(id_mask);
     }
   }
   // 1. the k best chunks, in order (every lane ends with them)
@@ -1743,10 +1769,17 @@ __device__ void gemm_topk_row(const CommitArgs& c, __amdgpu_buffer_rsrc_t tk, in
       bh = make_uint2(better ? Lst[n][0].x : bh.x, better ? Lst[n][0].y : bh.y);
       bn = better ? n : bn;
     }
+    // the best head: the largest maximum, then the lowest id.  Entries are real chunks (finite
+    // maxima) or empty (-inf, the all-ones id), and no chunk sits in two lists, so the winner is
+    // unique; the lowest-id reduction runs only when several heads share the maximum.
     const float m = wave_max(__uint_as_float(bh.x));
-    const int id = wave_allreduce_min(__uint_as_float(bh.x) == m ? (int)(bh.y & id_mask) : (int)id_mask);
-    const bool win = __uint_as_float(bh.x) == m && (int)(bh.y & id_mask) == id && id != (int)id_mask;
-    const uint64_t wl = __builtin_amdgcn_ballot_w64(win);
+    const bool top = __uint_as_float(bh.x) == m && (bh.y & id_mask) != id_mask;
+    uint64_t wl = __builtin_amdgcn_ballot_w64(top);
+    if (__builtin_popcountll(wl) > 1) {                   // (uniform)
+      const int id = wave_allreduce_min(top ? (int)(bh.y & id_mask) : (int)id_mask);
+      wl = __builtin_amdgcn_ballot_w64(top && (int)(bh.y & id_mask) == id);
+    }
+    const bool win = (wl >> lane) & 1ull;
     C[r] = chunk_empty(id_mask);
     if (wl) {
       const int w = __builtin_ctzll(wl);
@@ -1835,9 +1868,14 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
   const int j = lane & 15;
   const bool writer = TK ? lane == 0 : j == 0;              // one lane per row writes its outputs
   Stats t;
+  // with TK: the row's chunk lists, loaded right behind the statistics records
+  uint4 tl[TK ? kTopkListsPerLane : 1][kTopK / 2];
+  const __amdgpu_buffer_rsrc_t tk = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint4*>(tka.lists), 0, TK ? nrows_total * G * (kTopK * 8) : 0, 0x00020000);
   if (G <= kGroup) {
     const float4 v = record_load_after_kernel(rec, j < G && rin ? 16u * (unsigned)(row + j * nrows_total) : kOOB);
-    t = stats_row16_merge(stats_unpack(j < G ? v : stats_pack(stats_empty())));
+    if constexpr (TK) gemm_topk_load(tk, G, nrows_total, row, rin, tl);
+    t = stats_row16_merge(stats_unpack_if(v, j < G));
   } else {
     float4 v[kGroup];
 #pragma unroll
@@ -1845,9 +1883,10 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
       const int g = kGroup * j + k;
       v[k] = record_load_after_kernel(rec, g < G && rin ? 16u * (unsigned)(row + g * nrows_total) : kOOB);
     }
+    if constexpr (TK) gemm_topk_load(tk, G, nrows_total, row, rin, tl);
     Stats q[kGroup];
 #pragma unroll
-    for (int k = 0; k < kGroup; ++k) q[k] = kGroup * j + k < G ? stats_unpack(v[k]) : stats_empty();
+    for (int k = 0; k < kGroup; ++k) q[k] = stats_unpack_if(v[k], kGroup * j + k < G);
     t = stats_row16_merge(stats_tree(q));
   }
   // S >= 1 in exact arithmetic; the rounding of m*log2(e) may put 1/S a few ulps above 1
@@ -1857,10 +1896,8 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
         const_cast<void*>(tka.W), 0, (int)((unsigned)tka.V * (unsigned)tka.H * 2u), 0x00020000);
     const __amdgpu_buffer_rsrc_t hrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<void*>(tka.hidden), 0, (int)((unsigned)(c.B * c.L) * (unsigned)tka.H * 2u), 0x00020000);
-    const __amdgpu_buffer_rsrc_t tk = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint4*>(tka.lists), 0, nrows_total * G * (kTopK * 8), 0x00020000);
     __shared__ uint4 rc_area[TK ? kFinRowsTopk * kRcLdsBytes / 16 : 1];   // a recompute area per wavefront
-    gemm_topk_row(c, tk, G, nrows_total, row, rin, wrs, hrs, tka.H, tka.V, tka.id_bits, t.m1, 1.f / t.s,
+    gemm_topk_row(c, tl, G, row, rin, wrs, hrs, tka.H, tka.V, tka.id_bits, t.m1, 1.f / t.s,
                   rc_area + (TK ? wave * (kRcLdsBytes / 16) : 0));
   }
   if (!do_commit) {
