@@ -1350,20 +1350,21 @@ __device__ __forceinline__ void fold_tile(Stats& st, const f32x16 (&acc)[G::VB][
     st.m1 = mnew;
     if constexpr (TK) {
       // the chunk enters this lane's list (entries [i * 64], best first) where it beats the last
-      // entry: it is carried down the list, swapping with every entry it beats (chunks arrive in
-      // ascending id order, so it goes behind equal maxima)
+      // entry.  A lane meets its chunks in ascending id order, so the new chunk goes in front of
+      // the first entry with a smaller maximum (behind equal maxima: their ids are lower; empty
+      // entries hold -inf), and every entry from there on moves down one place.
       const bool enter = m > __uint_as_float(list[(kTopK - 1) * 64].x);
       if (__builtin_amdgcn_ballot_w64(enter)) {
         if (enter) {
-          const unsigned id_mask = (1u << id_bits) - 1u;
           uint2 carry = make_uint2(__float_as_uint(m),
                                    (unsigned)(v0 + 32 * vb + id) | (chunk_gap_code(m, m2, id_bits) << id_bits));
+          bool shift = false;
 #pragma unroll
           for (int i = 0; i < kTopK; ++i) {
             const uint2 e = list[i * 64];
-            const bool b = chunk_before(carry, e, id_mask);
-            list[i * 64] = make_uint2(b ? carry.x : e.x, b ? carry.y : e.y);
-            carry = make_uint2(b ? e.x : carry.x, b ? e.y : carry.y);
+            shift = shift | (m > __uint_as_float(e.x));
+            list[i * 64] = make_uint2(shift ? carry.x : e.x, shift ? carry.y : e.y);
+            carry = make_uint2(shift ? e.x : carry.x, shift ? e.y : carry.y);
           }
         }
       }
