@@ -219,6 +219,13 @@ def test_topk_workspace_sizes():
         nat.dlm_workspace_bytes(16, 32, 2048, 157184, nat.DLM_BF16) + 512 * 256 * 64
     assert nat.dlm_workspace_bytes_topk(5, 13, 256, 3001, nat.DLM_BF16, 8) == \
         256 + 512 * 24 * 16 + 96 * 256 * 2 + 65 * 16 + 512 * 24 * 64     # 24 tiles of 128: 24 workgroups
+    # the largest vocabulary of the GEMM head with chunk lists: V = 2^22 - 1 (22-bit ids, 128 rows
+    # in one 512-row group, 256 workgroups); at V = 2^22 W passes 2 GiB and the streaming plan
+    # takes the 128 rows (two 64-row groups, 128 ranges, 8 groups of ranges)
+    assert nat.dlm_workspace_bytes_topk(2, 64, 256, (1 << 22) - 1, nat.DLM_BF16, 8) == \
+        256 + 512 * 256 * 16 + 128 * 256 * 2 + 128 * 16 + 512 * 256 * 64
+    assert nat.dlm_workspace_bytes_topk(2, 64, 256, 1 << 22, nat.DLM_BF16, 8) == \
+        256 + 2 * 64 * 128 * 16 + 2 * 64 * 8 * 16 + 2 * 64 * 128 * 64 + 2 * 64 * 8 * 64
     for B, L, H, V, dt in [(1, 32, 2048, 126464, 1), (16, 32, 2048, 157184, 1), (1, 8, 64, 1024, 0)]:
         assert nat.dlm_workspace_bytes_topk(B, L, H, V, dt, 0) == nat.dlm_workspace_bytes(B, L, H, V, dt)
     assert nat.dlm_workspace_bytes_topk(1, 32, 2048, 126464, nat.DLM_BF16, 9) == 0

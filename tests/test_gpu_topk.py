@@ -117,6 +117,26 @@ def test_topk_token_stats(B, L, H, V, dtype, k):
     assert compared >= len(rows) // 2
 
 
+def test_topk_gemm_head_largest_vocabulary():
+    """The GEMM head's chunk entries pack the id and the gap code into 32 bits: at V = 2^22 - 1
+    the id takes 22 bits and the gap code keeps 6 mantissa bits, the coarsest it gets.  65 rows
+    (GEMM path, ragged last tile), sampled rows against the oracle."""
+    from decoding_step_amd import _native as nat
+    from decoding_step_amd.synth import BlockStream, make_weights
+    B, L, H, V, k = 5, 13, 256, (1 << 22) - 1, 8
+    say(f"gpu: top-k on the GEMM head at the largest vocabulary, B={B} L={L} H={H} V={V}")
+    W = make_weights(V, H, "bf16", seed=7)
+    h = BlockStream(W, B * L, 11, 30.0).hidden(0, 0)
+    conf, tok, gap, tt, tp = _stats_topk(h, W, B, L, k, nat.DLM_BF16)
+    _valid(tt, tp, V, k)
+    assert np.array_equal(tt[:, 0], tok)
+    assert np.array_equal(tp[:, 0], conf)
+    rows = np.array([0, 1, 17, 31, 32, 63, 64])
+    compared, exempt = _check_against_oracle(h, W, rows, k, tt[rows], tp[rows])
+    say(f"[top-k] {len(rows)} rows, {compared} ranks compared exactly, {exempt} within 1e-2 of a neighbour")
+    assert compared >= len(rows) // 2
+
+
 def test_topk_exact_ties_across_workgroups():
     """Copies of one vocabulary row give bit-equal logits wherever they sit (same K order), so
     they must come out adjacent and in id order: within a thread's stream (ids 16 apart), across
