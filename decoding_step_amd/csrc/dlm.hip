@@ -260,8 +260,10 @@ int head_event(const dlm_policy* pol, bool time_head, int i, hipStream_t stream)
   return DLM_OK;
 }
 
+// next_hidden (GEMM path without top-k, several steps per call): the finalizer launch also packs
+// the next step's hidden rows; prepacked: this step's were packed that way, so no pack launch.
 int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::CommitArgs c, bool commit,
-             bool time_head, size_t fixed_ticket_bytes = 0) {
+             bool time_head, size_t fixed_ticket_bytes = 0, const void* next_hidden = nullptr, bool prepacked = false) {
   Plan p;
   int rc = make_plan(pol->B, pol->L, pol->H, pol->V, pol->dtype, c.topk, &p, fixed_ticket_bytes);
   if (rc) return rc;
@@ -294,10 +296,13 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
   if (p.gemm) {
     void* packed = static_cast<char*>(pol->workspace) + p.packed_off;
     const int pack_waves = (a.M + 31) / 32 * (a.H / 64);   // (H % 256 == 0 on this path)
-    hipLaunchKernelGGL(dlm::pack_hidden_kernel, dim3((pack_waves + 3) / 4), dim3(256), 0, stream,
-                       static_cast<const uint4*>(hidden), static_cast<uint4*>(packed), a.M, a.H);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(DLM_ERR_HIP, "pack kernel launch: %s", hipGetErrorString(e));
+    hipError_t e = hipSuccess;
+    if (!prepacked) {
+      hipLaunchKernelGGL(dlm::pack_hidden_kernel, dim3((pack_waves + 3) / 4), dim3(256), 0, stream,
+                         static_cast<const uint4*>(hidden), static_cast<uint4*>(packed), a.M, a.H);
+      e = hipGetLastError();
+      if (e != hipSuccess) return fail(DLM_ERR_HIP, "pack kernel launch: %s", hipGetErrorString(e));
+    }
     dlm::GemmArgs g;
     g.hidden_packed = packed;
     g.packed_bytes = (unsigned)p.packed_bytes;
@@ -337,12 +342,19 @@ int run_step(const void* hidden, const void* W, const dlm_policy* pol, dlm::Comm
     tka.V = a.V;
     tka.id_bits = g.id_bits;
     float4* const row_out = reinterpret_cast<float4*>(static_cast<char*>(pol->workspace) + p.rowout_off);
+    dlm::PackArgs pk;                                     // the next step's pack, if any, after the parts
+    pk.h = static_cast<const uint4*>(next_hidden);
+    pk.hp = static_cast<uint4*>(packed);
+    pk.M = a.M;
+    pk.H = a.H;
+    pk.first_block = c.B * parts;
+    const int pack_blocks = next_hidden && !p.topk ? (pack_waves + 1) / 2 : 0;
     if (p.topk)
       hipLaunchKernelGGL(dlm::finalize_parts_kernel<true>, dim3(c.B * parts), dim3(64 * dlm::kFinRowsTopk), 0, stream,
-                         a.c, a.partials, p.G_v, p.n_rg * rows, a.ticket, row_out, tka);
+                         a.c, a.partials, p.G_v, p.n_rg * rows, a.ticket, row_out, tka, pk);
     else
-      hipLaunchKernelGGL(dlm::finalize_parts_kernel<false>, dim3(c.B * parts), dim3(128), 0, stream, a.c, a.partials,
-                         p.G_v, p.n_rg * rows, a.ticket, row_out, tka);
+      hipLaunchKernelGGL(dlm::finalize_parts_kernel<false>, dim3(c.B * parts + pack_blocks), dim3(128), 0, stream,
+                         a.c, a.partials, p.G_v, p.n_rg * rows, a.ticket, row_out, tka, pk);
     e = hipGetLastError();
     if (e != hipSuccess) return fail(DLM_ERR_HIP, "finalize kernel launch: %s", hipGetErrorString(e));
     return ok();
@@ -488,6 +500,9 @@ int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mas
   c.out_gap = policy->out_gap;
   int32_t* const topk_tokens0 = c.out_topk_tokens;
   float* const topk_prob0 = c.out_topk_prob;
+  // on the GEMM path without top-k, each step's finalizer also packs the next step's hidden rows
+  const bool chain_pack = p.gemm && !p.topk;
+  const char* const h0 = static_cast<const char*>(hidden_steps);
   for (int64_t n = 0; n < n_steps; ++n) {
     c.out_tokens = out_tokens_steps + n * rows;
     c.out_commit = out_commit_steps + n * rows;
@@ -495,7 +510,8 @@ int dlm_decode_steps(const void* hidden_steps, const void* W_vocab, uint8_t* mas
       c.out_topk_tokens = topk_tokens0 + (size_t)n * rows * c.topk;
       c.out_topk_prob = topk_prob0 ? topk_prob0 + (size_t)n * rows * c.topk : nullptr;
     }
-    rc = run_step(static_cast<const char*>(hidden_steps) + n * step_bytes, W_vocab, policy, c, true, false);
+    const void* next = chain_pack && n + 1 < n_steps ? h0 + (n + 1) * step_bytes : nullptr;
+    rc = run_step(h0 + n * step_bytes, W_vocab, policy, c, true, false, 0, next, chain_pack && n > 0);
     if (rc) return rc;  // only a failed launch can get here, after validation passed
   }
   return ok();

@@ -1256,10 +1256,9 @@ __device__ __forceinline__ uint2 chunk_empty(unsigned id_mask) { return make_uin
 // (rb * H/16 + kg) * 1 KB.  One wavefront packs four consecutive
 // fragments of one 32-row block: each of its four loads covers 8 rows x 128 contiguous bytes, and
 // each store writes 8 whole 128-byte lines of the output (lanes l%8 == u, 8 rows apart).
-// Grid: ceil(M/32) * H/64 wavefronts, four per workgroup (H % 64 == 0).
-__global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4* hp, int M, int H) {
+// ceil(M/32) * H/64 wavefronts in all (H % 64 == 0); wavefront w of them packs its four fragments.
+__device__ __forceinline__ void pack_hidden_wave(const uint4* h, uint4* hp, int M, int H, int w, int lane) {
   const int KG = H / 16;
-  const int w = gid() * 4 + (lid() >> 6), lane = lid() & 63;
   const int quads = KG / 4;
   if (w >= ((M + 31) / 32) * quads) return;
   const int rb = w / quads, kg0 = 4 * (w % quads);
@@ -1276,6 +1275,21 @@ __global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4*
     hp[((unsigned)(rb * KG + kg0 + (u >> 1)) << 6) + (unsigned)(i + 32 * (u & 1))] = v[j];
   }
 }
+
+// Grid: the pack's wavefronts, four per workgroup.
+__global__ __launch_bounds__(256) void pack_hidden_kernel(const uint4* h, uint4* hp, int M, int H) {
+  pack_hidden_wave(h, hp, M, H, gid() * 4 + (lid() >> 6), lid() & 63);
+}
+
+// The next step's pack riding on a finalizer launch (several steps per call): workgroups from
+// first_block on pack, two wavefronts each.  The packed rows are free once the step's GEMM kernel
+// has ended, which the finalizer's launch follows; the next GEMM kernel follows the finalizer.
+struct PackArgs {
+  const uint4* h;               // the next step's hidden rows, [M][H] bf16
+  uint4* hp;                    // the packed copy in the workspace
+  int M, H;
+  int first_block;              // the finalizer's own workgroups come first; past the grid: no pack
+};
 
 __device__ __forceinline__ f32x16 mma32(uint4 a, uint4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
@@ -1853,7 +1867,11 @@ struct GemmTopkArgs {           // the export's inputs on the GEMM path (TK fina
 template <bool TK>
 __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c, const float4* records, int G,
                                                              int nrows_total, unsigned* tickets, float4* row_out,
-                                                             const GemmTopkArgs tka) {
+                                                             const GemmTopkArgs tka, const PackArgs pk) {
+  if (gid() >= pk.first_block) {                          // (uniform) a pack workgroup
+    pack_hidden_wave(pk.h, pk.hp, pk.M, pk.H, (gid() - pk.first_block) * 2 + (lid() >> 6), lid() & 63);
+    return;
+  }
   constexpr unsigned kOOB = 0x80000000u;
   constexpr int kRows = TK ? kFinRowsTopk : kFinRows;
   const int parts = (c.L + kRows - 1) / kRows;
