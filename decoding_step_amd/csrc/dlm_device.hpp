@@ -1895,6 +1895,22 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
     const float4 v = record_load_after_kernel(rec, j < G && rin ? 16u * (unsigned)(row + j * nrows_total) : kOOB);
     if constexpr (TK) gemm_topk_load(tk, G, nrows_total, row, rin, tl);
     t = stats_row16_merge(stats_unpack_if(v, j < G));
+  } else if constexpr (TK) {
+    // one row per wavefront: lane j + 16qq merges records 16j + 4qq .. +3 in registers, the
+    // quarters of each group pairwise across the 16-lane rows, then the groups: the same tree as
+    // one lane per group (stats_merge is symmetric), with four records per lane instead of 16
+    const int qq = lane >> 4;
+    float4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int g = kGroup * j + 4 * qq + k;
+      v[k] = record_load_after_kernel(rec, g < G && rin ? 16u * (unsigned)(row + g * nrows_total) : kOOB);
+    }
+    gemm_topk_load(tk, G, nrows_total, row, rin, tl);
+    Stats q[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = stats_unpack_if(v[k], kGroup * j + 4 * qq + k < G);
+    t = stats_row16_merge(stats_merge_rows<32>(stats_merge_rows<16>(stats_tree(q))));
   } else {
     float4 v[kGroup];
 #pragma unroll
@@ -1902,7 +1918,6 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
       const int g = kGroup * j + k;
       v[k] = record_load_after_kernel(rec, g < G && rin ? 16u * (unsigned)(row + g * nrows_total) : kOOB);
     }
-    if constexpr (TK) gemm_topk_load(tk, G, nrows_total, row, rin, tl);
     Stats q[kGroup];
 #pragma unroll
     for (int k = 0; k < kGroup; ++k) q[k] = stats_unpack_if(v[k], kGroup * j + k < G);
