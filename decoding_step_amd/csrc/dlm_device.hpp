@@ -1906,7 +1906,7 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
       const int g = kGroup * j + 4 * qq + k;
       v[k] = record_load_after_kernel(rec, g < G && rin ? 16u * (unsigned)(row + g * nrows_total) : kOOB);
     }
-    gemm_topk_load(tk, G, nrows_total, row, rin, tl);
+    if constexpr (TK) gemm_topk_load(tk, G, nrows_total, row, rin, tl);
     Stats q[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) q[k] = stats_unpack_if(v[k], kGroup * j + 4 * qq + k < G);
