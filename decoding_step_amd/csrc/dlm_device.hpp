@@ -1653,10 +1653,11 @@ __global__ __launch_bounds__(GemmR512::Threads) void gemm_r512_topk_tail_kernel(
 //     sequence to finish (a wrapping counter per sequence, so a zeroed workspace is zero again
 //     after every call) commits the sequence from the published values.
 // records: [G][nrows_total] (the GEMM kernels' layout).  Grid: B x ceil(L / kFinRows) workgroups of
-// 128 threads.  tickets: [B] counters; row_out: [B*L] 16-byte values.
+// 128 threads, then the pack workgroups of PackArgs, if any.  tickets: [B] counters; row_out:
+// [B*L] 16-byte values.
 // With TK (top-k export after gemm_r512_topk_kernel) a workgroup takes kFinRowsTopk rows, one per
-// wavefront (its four 16-lane rows merge the same row's statistics, with the same tree), and each
-// wavefront also writes its row's export (gemm_topk_row).
+// wavefront (lane j + 16q merges records 16j + 4q .. +3, the same tree), and each wavefront also
+// writes its row's export (gemm_topk_row).
 constexpr int kFinRows = 8;
 constexpr int kFinRowsTopk = 2;   // with the top-k export: one row per wavefront, two per workgroup
 
