@@ -243,6 +243,27 @@ def time_shard_share(wl, W, hidden, seq, warmup, steps, dev, G):
     return total, ev[0].elapsed_time(ev[1]) / 1e3, ev[1].elapsed_time(ev[2]) / 1e3, cuts[1] - cuts[0]
 
 
+def time_vendor_gemm(Wd, hidden, warmup, steps):
+    """The bare contraction of the same rows with the same W by the vendor library: torch.mm,
+    which ROCm's torch hands to hipBLASLt, writing the [B*L][V] logits to HBM in bf16 and
+    computing no statistics.  A reference point for the fused head, not part of the step."""
+    import torch
+    n, B, L, H = hidden.shape
+    x = hidden.reshape(n, B * L, H)
+    out = torch.empty((B * L, Wd.shape[0]), dtype=Wd.dtype, device=Wd.device)
+    for i in range(warmup):
+        torch.mm(x[i % n], Wd.t(), out=out)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        torch.mm(x[i % n], Wd.t(), out=out)
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps * 1e3          # us per call
+
+
 def cpu_baseline(wl, W, budget_s=20.0, topk=0):
     """The oracle as it stands, on the first steps of the same workload, on this host's cores
     (with the top-k export, the oracle's topk_candidates over the same rows is part of a step)."""
@@ -310,6 +331,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time")
     ap.add_argument("--topk", type=int, default=0,
                     help="also export the k best candidates of every row (0 = off, at most 8)")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="also time the vendor library's plain GEMM (torch.mm -> hipBLASLt) on the same "
+                         "rows and W, bf16 logits out, no statistics (GEMM-shaped workloads only)")
     ap.add_argument("--shards", type=int, default=1,
                     help="time one GPU's share of a head split over this many vocabulary shards "
                          "(shard kernel + merge of the shards' records; the exchange is not timed)")
@@ -336,6 +360,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     wl = WORKLOADS[args.workload]
+    if args.vendor_gemm and (args.shards > 1 or not (wl.dtype == "bf16" and wl.B * wl.L > 64 and wl.H % 256 == 0)):
+        ap.error("--vendor-gemm needs a GEMM-shaped workload (bf16, B*L > 64) and no --shards")
     print(f"[bench] workload {wl.name}: generating W ({wl.V}x{wl.H} {wl.dtype})", file=sys.stderr, flush=True)
     W = make_weights(wl.V, wl.H, wl.dtype)
     Wd = to_device(W, dev)
@@ -430,6 +456,13 @@ def main():
         "blocks_completed": blocks,
         "host_wall_s": wall,
     }
+    if args.vendor_gemm:
+        print("[bench] timing the vendor GEMM on the same operands", file=sys.stderr, flush=True)
+        us = time_vendor_gemm(Wd, hidden, args.warmup, args.steps)
+        out["vendor_gemm"] = {
+            "kernel": "torch.mm (hipBLASLt): [B*L][H] x [H][V] -> bf16 logits in HBM, no statistics",
+            "us": us, "tflops": flops / (us * 1e-6) / 1e12, "frac": flops / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+            "fused_head_speedup": None if head is None else us / float(np.mean(head))}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(wl, W, args.cpu_budget, args.topk)
