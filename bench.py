@@ -264,6 +264,45 @@ def time_vendor_gemm(Wd, hidden, warmup, steps):
     return t0.elapsed_time(t1) / steps * 1e3          # us per call
 
 
+def measure_ceilings(dev):
+    """Practical ceilings of this GPU by vendor routines, beside the published peaks: a 2 GiB
+    device-to-device copy (HBM read + write), a float32-accumulated sum over 2 GiB of bf16 (HBM
+    read), and torch.mm of two 8192 x 8192 bf16 matrices (hipBLASLt)."""
+    import torch
+
+    def per_call(f, n, warm=5):
+        for _ in range(warm):
+            f()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(n):
+            f()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n * 1e-3
+
+    nbytes = 1 << 31
+    a = torch.ones(nbytes // 2, dtype=torch.bfloat16, device=dev)
+    b = torch.empty_like(a)
+    s_copy = per_call(lambda: b.copy_(a), 20)
+    s_sum = per_call(lambda: a.sum(dtype=torch.float32), 20)
+    del b
+    n = 8192
+    x = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    y = torch.randn(n, n, dtype=torch.bfloat16, device=dev)
+    z = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    s_mm = per_call(lambda: torch.mm(x, y, out=z), 20)
+    return {
+        "copy_GBps": 2 * nbytes / s_copy / 1e9, "copy_frac_of_hbm_peak": 2 * nbytes / s_copy / 1e9 / HBM_PEAK_GBS,
+        "read_sum_GBps": nbytes / s_sum / 1e9, "read_sum_frac_of_hbm_peak": nbytes / s_sum / 1e9 / HBM_PEAK_GBS,
+        "mm8192_bf16_TFLOPs": 2 * n ** 3 / s_mm / 1e12,
+        "mm8192_frac_of_mfma_peak": 2 * n ** 3 / s_mm / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+        "note": "torch copy_, sum(dtype=float32) and mm (hipBLASLt) on this GPU; 20 calls after 5 untimed",
+    }
+
+
 def cpu_baseline(wl, W, budget_s=20.0, topk=0):
     """The oracle as it stands, on the first steps of the same workload, on this host's cores
     (with the top-k export, the oracle's topk_candidates over the same rows is part of a step)."""
@@ -334,6 +373,9 @@ def main():
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="also time the vendor library's plain GEMM (torch.mm -> hipBLASLt) on the same "
                          "rows and W, bf16 logits out, no statistics (GEMM-shaped workloads only)")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="only measure this GPU's practical ceilings with vendor routines (HBM copy and read, "
+                         "an 8192^3 bf16 GEMM) and print them as one JSON line")
     ap.add_argument("--shards", type=int, default=1,
                     help="time one GPU's share of a head split over this many vocabulary shards "
                          "(shard kernel + merge of the shards' records; the exchange is not timed)")
@@ -359,6 +401,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     dev = torch.device("cuda:0")
+    if args.ceilings:
+        print(json.dumps({"ceilings": measure_ceilings(dev), "hbm_peak_GBps": HBM_PEAK_GBS,
+                          "mfma_bf16_peak_TFLOPs": MFMA_BF16_PEAK_TFLOPS}), flush=True)
+        return
     wl = WORKLOADS[args.workload]
     if args.vendor_gemm and (args.shards > 1 or not (wl.dtype == "bf16" and wl.B * wl.L > 64 and wl.H % 256 == 0)):
         ap.error("--vendor-gemm needs a GEMM-shaped workload (bf16, B*L > 64) and no --shards")
