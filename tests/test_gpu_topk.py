@@ -283,41 +283,117 @@ def test_topk_step_on_the_batched_workload():
         assert compared >= 2 and c >= len(rows) * 4
 
 
-def test_topk_in_decode_steps():
-    """dlm_decode_steps writes one export per step; each equals the single-step call's."""
+def _topk_steps_setup(name, k, n):
+    """A Decoder with the export on, and n steps of the workload one call each (each sequence
+    advancing to its next block when its mask empties): the staged hidden blocks and each step's
+    export."""
     from decoding_step_amd import _native as nat
     from decoding_step_amd.device import Decoder, new_credit, to_device
     from decoding_step_amd.synth import BlockStream, make_weights
     from decoding_step_amd.workloads import WORKLOADS
-    say("gpu: dlm_decode_steps with top-k, credit_b1_l32, 4 steps")
-    wl = WORKLOADS["credit_b1_l32"]
-    k, n = 5, 4
+    wl = WORKLOADS[name]
     W = make_weights(wl.V, wl.H, wl.dtype)
     Wd = to_device(W)
     seq = [(p.kind, p.threshold, p.decay, p.max_depth) for p in wl.policies]
     dec = Decoder(Wd, wl.B, wl.L, seq, flags=nat.DLM_AUTO_ADVANCE, topk=k)
-    bs = BlockStream(W, wl.L, wl.seeds[0], wl.a_max, wl.redraw_p[0])
+    streams = [BlockStream(W, wl.L, s, wl.a_max, rp) for s, rp in zip(wl.seeds, wl.redraw_p)]
     mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device="cuda")
     credit = new_credit(wl.B, wl.L)
-    pos, hs, ref_tt, ref_tp = [0, 0], [], [], []
+    pos = [[0, 0] for _ in range(wl.B)]
+    hs, ref = [], {"tok": [], "com": [], "tt": [], "tp": []}
     for _ in range(n):
-        h = bs.hidden(*pos)[None]
+        h = np.stack([streams[b].hidden(*pos[b]) for b in range(wl.B)])
         hs.append(h)
         dec.step(to_device(h), mask, credit)
-        ref_tt.append(dec.topk_tokens.cpu().numpy().copy())
-        ref_tp.append(dec.topk_prob.cpu().numpy().copy())
-        pos = [pos[0] + 1, 0] if not mask.cpu().numpy().any() else [pos[0], pos[1] + 1]
-    mask.fill_(1)
-    credit.copy_(new_credit(wl.B, wl.L))
-    tok = torch.empty((n, wl.B, wl.L), dtype=torch.int32, device="cuda")
-    com = torch.empty((n, wl.B, wl.L), dtype=torch.uint8, device="cuda")
+        ref["tok"].append(dec.out_tokens.cpu().numpy().copy())
+        ref["com"].append(dec.out_commit.cpu().numpy().copy())
+        ref["tt"].append(dec.topk_tokens.cpu().numpy().copy())
+        ref["tp"].append(dec.topk_prob.cpu().numpy().copy())
+        m = mask.cpu().numpy()
+        for b in range(wl.B):
+            pos[b] = [pos[b][0] + 1, 0] if not m[b].any() else [pos[b][0], pos[b][1] + 1]
+    ref = {key: np.stack(v) for key, v in ref.items()}
+    ref["mask"] = mask.cpu().numpy()
+    return wl, dec, to_device(np.stack(hs)), ref
+
+
+def _topk_steps_buffers(wl, k, n):
+    tok = torch.full((n, wl.B, wl.L), -5, dtype=torch.int32, device="cuda")
+    com = torch.full((n, wl.B, wl.L), 3, dtype=torch.uint8, device="cuda")
     tt = torch.full((n, wl.B, wl.L, k), -9, dtype=torch.int32, device="cuda")
     tp = torch.full((n, wl.B, wl.L, k), -9.0, dtype=torch.float32, device="cuda")
-    dec.steps(to_device(np.stack(hs)), mask, credit, tok, com, tt, tp)
+    return tok, com, tt, tp
+
+
+def _topk_steps_check(ref, mask, tok, com, tt, tp, label):
+    np.testing.assert_array_equal(tok.cpu().numpy(), ref["tok"], err_msg=f"{label}: tokens")
+    np.testing.assert_array_equal(com.cpu().numpy(), ref["com"], err_msg=f"{label}: commits")
+    np.testing.assert_array_equal(mask.cpu().numpy(), ref["mask"], err_msg=f"{label}: mask")
+    np.testing.assert_array_equal(tt.cpu().numpy(), ref["tt"], err_msg=f"{label}: export tokens")
+    np.testing.assert_array_equal(tp.cpu().numpy(), ref["tp"], err_msg=f"{label}: export probabilities")
+
+
+@pytest.mark.parametrize("name,k,n", [
+    ("credit_b1_l32", 5, 4),      # streaming head: one launch per step
+    ("mixed_b16_l32", 8, 3),      # GEMM-shaped head: pack, head with chunk lists, finalize per step
+])
+def test_topk_in_decode_steps(name, k, n):
+    """dlm_decode_steps writes one export per step; each equals the single-step call's, and the
+    Decoder's own export buffers are back in the policy afterwards."""
+    from decoding_step_amd.device import new_credit
+    say(f"gpu: dlm_decode_steps with top-{k}, {name}, {n} steps")
+    wl, dec, hidden_steps, ref = _topk_steps_setup(name, k, n)
+    mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device="cuda")
+    credit = new_credit(wl.B, wl.L)
+    tok, com, tt, tp = _topk_steps_buffers(wl, k, n)
+    dec.steps(hidden_steps, mask, credit, tok, com, tt, tp)
     torch.cuda.synchronize()
-    assert np.array_equal(tt.cpu().numpy(), np.stack(ref_tt))
-    assert np.array_equal(tp.cpu().numpy(), np.stack(ref_tp))
-    # the Decoder's own buffers are back in the policy afterwards
-    dec.step(to_device(hs[0]), torch.ones_like(mask), new_credit(wl.B, wl.L))
+    _topk_steps_check(ref, mask, tok, com, tt, tp, name)
+    dec.step(hidden_steps[0], torch.ones_like(mask), new_credit(wl.B, wl.L))
     torch.cuda.synchronize()
-    assert np.array_equal(dec.topk_tokens.cpu().numpy(), ref_tt[0])
+    assert np.array_equal(dec.topk_tokens.cpu().numpy(), ref["tt"][0])
+    say(f"[{name}] {n} steps' exports equal the single-step calls'")
+
+
+@pytest.mark.parametrize("name,k,n", [
+    ("threshold_b1_l32", 8, 3),   # streaming head
+    ("mixed_b16_l32", 8, 3),      # GEMM-shaped head
+])
+def test_topk_decode_steps_inside_a_graph(name, k, n):
+    """dlm_decode_steps with the export on, captured in a HIP graph and replayed three times with
+    eager work between the replays: every replay equals the single-step calls."""
+    from decoding_step_amd.device import new_credit
+    say(f"gpu: dlm_decode_steps with top-{k}, {name}, captured in a HIP graph, replayed 3 times")
+    wl, dec, hidden_steps, ref = _topk_steps_setup(name, k, n)
+    mask = torch.ones((wl.B, wl.L), dtype=torch.uint8, device="cuda")
+    credit = new_credit(wl.B, wl.L)
+    credit0 = credit.clone()
+    tok, com, tt, tp = _topk_steps_buffers(wl, k, n)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                     # warm-up on the capture stream
+        dec.policy.set_stream(side)
+        dec.steps(hidden_steps, mask, credit, tok, com, tt, tp)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    _topk_steps_check(ref, mask, tok, com, tt, tp, f"{name} eager")
+    g = torch.cuda.CUDAGraph()
+    mask.fill_(1)
+    credit.copy_(credit0)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        dec.policy.set_stream(torch.cuda.current_stream())
+        dec.steps(hidden_steps, mask, credit, tok, com, tt, tp)
+    dec.policy.set_stream(None)
+    for rep in range(3):
+        mask.fill_(1)                                  # eager work between replays
+        credit.copy_(credit0)
+        tok.fill_(-5)
+        com.fill_(3)
+        tt.fill_(-9)
+        tp.fill_(-9.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        _topk_steps_check(ref, mask, tok, com, tt, tp, f"{name} replay {rep}")
+    say(f"[{name}] 3 replays with the export equal the single-step calls")
