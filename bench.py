@@ -385,7 +385,7 @@ def main():
     if not 1 <= args.shards <= 256 or (args.shards > 1 and args.topk):
         ap.error("--shards must be in 1..256, and the shard calls have no top-k export")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the step shards by sequence or by vocabulary range; see the design notes).", file=sys.stderr)
         sys.exit(2)
 
