@@ -72,6 +72,7 @@ __host__ __device__ constexpr size_t lds_bytes_topk(int NMB) {
   return lds_bytes(NMB) > (size_t)256 * NMB * (16 + DLM_MAX_TOPK * 8) ? lds_bytes(NMB)
                                                                         : (size_t)256 * NMB * (16 + DLM_MAX_TOPK * 8);
 }
+static_assert(lds_bytes_topk(1) >= (size_t)kRowsPerStage * 20, "the finalize stage with top-k lists fits");
 
 struct StepArgs {
   const void* hidden;  // [M][H]
@@ -676,7 +677,10 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
 // The per-row outputs (confidence, gap, and the candidates without a commit) are written after the
 // commits: a wavefront's vector-memory counter also counts its stores, so a store issued before a
 // commit would make the commit's wait for its loaded state wait for the store's acknowledgement.
-// Called by a whole workgroup; `smem` needs kRowsPerStage * 12 bytes.
+// TK (GROUPED only): each row's 16 lanes also merge the groups' top-k lists and write the export.
+// A wavefront that commits a sequence merges its rows' lists before the commits; the others merge
+// theirs after the barrier, while the commits run (each row's maximum and 1/sum wait in LDS).
+// Called by a whole workgroup; `smem` needs kRowsPerStage * 12 bytes (20 with TK).
 // ----------------------------------------------------------------------------------------------
 __device__ __forceinline__ void finalize_row(const CommitArgs& c, const Stats& t, int row, int rr, float* s_conf,
                                              int* s_tok, float* s_gap) {
@@ -703,51 +707,92 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
   float* s_conf = reinterpret_cast<float*>(smem);
   int* s_tok = reinterpret_cast<int*>(smem) + kRowsPerStage;
   float* s_gap = reinterpret_cast<float*>(smem) + 2 * kRowsPerStage;
+  float* s_m1 = reinterpret_cast<float*>(smem) + 3 * kRowsPerStage;     // TK: each row's maximum
+  float* s_inv_s = reinterpret_cast<float*>(smem) + 4 * kRowsPerStage;  // TK: each row's 1/sum
   const int seq_per_stage = max(1, kRowsPerStage / c.L);
+  auto rec_off = [&](int r_first, int nrows, int rr, int j) {
+    const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
+    return j < G && rr < nrows ? src + 16u * (unsigned)(j * rs_g) : 0x80000000u;
+  };
+  auto list_off = [](unsigned o, int q) { return o == 0x80000000u ? o : o * (unsigned)(kTopK / 2) + 16u * q; };
   for (int b0 = b_begin; b0 < b_end; b0 += seq_per_stage) {
     const int b1 = min(b_end, b0 + seq_per_stage);
     const int r_first = b0 * c.L, nrows = (b1 - b0) * c.L;
-    // 4 rows per wavefront pass, one per 16-lane row; lane j of a row takes group j
+    // GROUPED: one record per lane, two passes of 4 rows per iteration (rows rr0 + 32h + lane/16,
+    // lane j taking group j), both passes' loads issued before the first merge, so up to 64 rows
+    // cost one round trip
+    const bool commits = do_commit && !c.out_records && wave < b1 - b0;   // (uniform)
+    float4 tl[TK ? 2 : 1][kTopK / 2];                     // TK: the iteration's top-k lists
+    auto stats_load = [&](int rr0, float4 (&v)[2]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned o = rec_off(r_first, nrows, rr0 + h * kWaves * 4 + (lane >> 4), lane & 15);
+        v[h] = IN_KERNEL ? record_load(rec, o) : record_load_after_kernel(rec, o);
+      }
+    };
+    auto lists_load = [&](int rr0) {                      // (64 bytes at [row][group] in trec)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned o = rec_off(r_first, nrows, rr0 + h * kWaves * 4 + (lane >> 4), lane & 15);
+#pragma unroll
+        for (int q = 0; q < kTopK / 2; ++q) tl[h][q] = record_load(trec, list_off(o, q));
+      }
+    };
+    auto merge_lists = [&](int rr0, int h, float m1, float inv_s) {   // the row's 16 lanes; the export
+      const int rr = rr0 + h * kWaves * 4 + (lane >> 4), j = lane & 15;
+      TopK mine, best;
+      if (j < G) {
+        topk_from_records(mine, tl[h]);
+      } else {
+        topk_clear(mine);
+      }
+      topk_row16_merge(mine, best);
+      if (rr < nrows) topk_write_row(c, best, r_first + rr, j, m1, inv_s);
+    };
     if constexpr (GROUPED) {
-      // one record per lane: two passes per iteration, both loads before the first merge, so
-      // up to 64 rows cost one round trip.  With TK the lane also loads its group's merged
-      // top-k list (64 bytes at [row][group] in trec) and the row's 16 lanes merge the lists.
-      for (int rr0 = wave * 4; rr0 < nrows; rr0 += 2 * kWaves * 4) {
+      auto stats_pass = [&](int rr0, const float4 (&v)[2]) {
         const int j = lane & 15;
-        float4 v[2];
-        float4 e[TK ? 2 : 1][kTopK / 2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int rr = rr0 + h * kWaves * 4 + (lane >> 4);
-          const unsigned src = (unsigned)((size_t)(r_first + (rr < nrows ? rr : 0)) * rs_row * 16);
-          const unsigned o = j < G && rr < nrows ? src + 16u * (unsigned)(j * rs_g) : 0x80000000u;
-          v[h] = IN_KERNEL ? record_load(rec, o) : record_load_after_kernel(rec, o);
-          if constexpr (TK) {
-#pragma unroll
-            for (int q = 0; q < kTopK / 2; ++q)
-              e[h][q] = record_load(trec, o == 0x80000000u ? o : o * (unsigned)(kTopK / 2) + 16u * q);
-          }
-        }
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const int rr = rr0 + h * kWaves * 4 + (lane >> 4);
           if (rr0 + h * kWaves * 4 >= nrows) break;   // (uniform: no row of this pass exists)
           const Stats t = stats_row16_merge(stats_unpack(j < G ? v[h] : stats_pack(stats_empty())));
-          if (rr < nrows && j == 0) finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
-          if constexpr (TK) {
-            TopK mine, best;
-            if (j < G) {
-              topk_from_records(mine, e[h]);
-            } else {
-              topk_clear(mine);
+          if (rr < nrows && j == 0) {
+            finalize_row(c, t, r_first + rr, rr, s_conf, s_tok, s_gap);
+            if constexpr (TK) {
+              s_m1[rr] = t.m1;
+              s_inv_s[rr] = 1.f / t.s;
             }
-            topk_row16_merge(mine, best);
-            if (rr < nrows) topk_write_row(c, best, r_first + rr, j, t.m1, 1.f / t.s);
+          }
+          if constexpr (TK) {
+            if (commits) merge_lists(rr0, h, t.m1, 1.f / t.s);
           }
         }
+      };
+      int rr0 = wave * 4;
+      if constexpr (TK) {
+        // The first iteration is straight-line code: its lists are loaded right behind its
+        // statistics records, and since loads return in order, the statistics merge waits for
+        // the records only.  (A branch between the two would leave the compiler's wait counts
+        // assuming the worst, so the merge would wait for the lists too.)
+        float4 v[2];
+        stats_load(rr0, v);
+        __builtin_amdgcn_sched_barrier(0);
+        lists_load(rr0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (rr0 < nrows) stats_pass(rr0, v);
+        rr0 += 2 * kWaves * 4;
+      }
+      for (; rr0 < nrows; rr0 += 2 * kWaves * 4) {
+        float4 v[2];
+        stats_load(rr0, v);
+        if constexpr (TK) {
+          if (commits) lists_load(rr0);
+        }
+        stats_pass(rr0, v);
       }
     } else
-    for (int rr0 = wave * 4; rr0 < nrows; rr0 += kWaves * 4) {
+    for (int rr0 = wave * 4; rr0 < nrows; rr0 += kWaves * 4) {   // 4 rows per pass, one per 16-lane row
       const int rr = rr0 + (lane >> 4), j = lane & 15;
       const bool rin = rr < nrows;
       const unsigned src = (unsigned)((size_t)(r_first + (rin ? rr : 0)) * rs_row * 16);
@@ -781,6 +826,21 @@ __device__ void finalize_sequences(const CommitArgs& c, __amdgpu_buffer_rsrc_t r
         const bool in = lane < c.L;
         const SeqState sq = b == pre_b ? pre : load_seq_state(c, b);
         commit_sequence(c, b, in ? s_conf[off] : 0.f, in ? s_tok[off] : 0, sq);
+      }
+    }
+    if constexpr (GROUPED && TK) {
+      // the wavefronts that commit nothing merge their rows' lists now, beside the commits
+      if (!commits) {
+        for (int rr0 = wave * 4; rr0 < nrows; rr0 += 2 * kWaves * 4) {
+          if (rr0 != wave * 4) lists_load(rr0);           // (the first iteration's are loaded)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int rr = rr0 + h * kWaves * 4 + (lane >> 4);
+            if (rr0 + h * kWaves * 4 >= nrows) break;   // (uniform)
+            const int rc = rr < nrows ? rr : nrows - 1;
+            merge_lists(rr0, h, s_m1[rc], s_inv_s[rc]);
+          }
+        }
       }
     }
     if (!c.out_records) {
