@@ -501,7 +501,7 @@ __device__ __forceinline__ uint64_t hierarchical_commit(uint64_t U, float conf, 
 // sequence's rule and early-stop state: loading them here lets a caller prefetch all of it while
 // it waits for something else (the rule lookup is two dependent reads of the argument block).
 struct SeqState {
-  bool masked;
+  int mask;   // the position's mask byte as loaded (0 past L), tested only when the commit needs it
   int st[DLM_CREDIT_SLOTS];
   float sc[DLM_CREDIT_SLOTS];
   Rule rule;
@@ -512,9 +512,14 @@ __device__ __forceinline__ SeqState load_seq_state(const CommitArgs& a, int b) {
   const int l = __lane_id();
   const size_t row = (size_t)b * a.L + l;
   SeqState s;
-  s.rule = a.rules[a.rule_of[b]];
+  // The rule index is a byte of the argument block (4-byte aligned array): reading its whole
+  // word lets a wavefront-uniform b go through scalar loads, so the rule costs no vector-memory
+  // round trip ahead of the sequence's own state.
+  unsigned ro;
+  __builtin_memcpy(&ro, __builtin_assume_aligned(a.rule_of + 4 * (b >> 2), 4), 4);
+  s.rule = a.rules[(ro >> (8 * (b & 3))) & 0xffu];
   s.done = a.seq_done ? (int)a.seq_done[b] : DLM_SEQ_RUNNING;
-  s.masked = l < a.L && a.mask[row] != 0;
+  s.mask = l < a.L ? (int)a.mask[row] : 0;
 #pragma unroll
   for (int i = 0; i < DLM_CREDIT_SLOTS; ++i) {
     s.st[i] = -1;
@@ -557,7 +562,7 @@ __device__ void commit_sequence(const CommitArgs& a, int b, float conf, int tok,
     return;
   }
 
-  bool masked = in_state.masked;
+  bool masked = in_state.mask != 0;
   uint64_t U = ballot(masked);
   const bool advance = U == 0ull && (a.flags & DLM_AUTO_ADVANCE);
   if (advance) {
@@ -1165,15 +1170,15 @@ __global__ __launch_bounds__(kThreads) void step_kernel(const StepArgs a) {
   __syncthreads();
   const CommitArgs& c = a.c;
   const bool do_commit = (c.flags & kFlagCommit) != 0;
-  if (tid == 0) {
-    const unsigned total = (unsigned)(a.n_rg * a.nq);
-    const unsigned prev = __builtin_amdgcn_atomic_inc32(a.ticket, total - 1, __ATOMIC_RELAXED, "agent");
-    s_last = prev == total - 1;
-  }
   // While the counter answers, each wavefront fetches the state of the sequence it would commit
-  // first (only the last workgroup uses it; the others drop it).
+  // first (only the last workgroup uses it; the others drop it): the loads go out after the
+  // counter's increment and before the wait for its answer.
+  const unsigned total = (unsigned)(a.n_rg * a.nq);
+  unsigned prev = 0;
+  if (tid == 0) prev = __builtin_amdgcn_atomic_inc32(a.ticket, total - 1, __ATOMIC_RELAXED, "agent");
   SeqState pre;
   if (do_commit && wave < c.B) pre = load_seq_state(c, wave);
+  if (tid == 0) s_last = prev == total - 1;
   __syncthreads();
   if (!s_last) return;
 
@@ -2014,12 +2019,12 @@ __global__ __launch_bounds__(128) void finalize_parts_kernel(const CommitArgs c,
   __builtin_amdgcn_s_waitcnt(0);                          // published before this part is counted
   __syncthreads();
   __shared__ int s_last;
-  if (tid == 0) {
-    const unsigned prev = __builtin_amdgcn_atomic_inc32(tickets + b, (unsigned)(parts - 1), __ATOMIC_RELAXED, "agent");
-    s_last = prev == (unsigned)(parts - 1);
-  }
-  SeqState pre;                                           // (used by the last part only)
+  // the sequence's state is fetched while the counter answers (used by the last part only)
+  unsigned prev = 0;
+  if (tid == 0) prev = __builtin_amdgcn_atomic_inc32(tickets + b, (unsigned)(parts - 1), __ATOMIC_RELAXED, "agent");
+  SeqState pre;
   if (wave == 0) pre = load_seq_state(c, b);
+  if (tid == 0) s_last = prev == (unsigned)(parts - 1);
   __syncthreads();
   if (!s_last || wave != 0) return;
   const bool in = lane < c.L;
