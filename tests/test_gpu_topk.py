@@ -93,6 +93,8 @@ def _valid(tok, prob, V, k):
     (5, 13, 256, 3001, "bf16", 8),         # 65 rows on the GEMM-shaped head (512-row group, mostly padding)
     (3, 32, 256, 5, "bf16", 8),            # fewer tokens than k on the GEMM-shaped head
     (8, 32, 256, 20011, "f32", 6),         # 256 float32 rows: the streaming head with the fold
+    (1, 32, 2048, 126464, "bf16", 1),      # k = 1 on the streaming head: the export is the candidate
+    (16, 32, 256, 5003, "bf16", 1),        # k = 1 on the GEMM-shaped head
 ])
 def test_topk_token_stats(B, L, H, V, dtype, k):
     from decoding_step_amd import _native as nat
